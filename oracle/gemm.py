@@ -1,0 +1,177 @@
+"""Reference FP8 block-scaled NT GEMMs in fp64.  Test infrastructure only.
+
+What is computed (D = A . B^T with block scales):
+
+    D[m, n] = sum over K slabs kb of
+              ( sum_{k in slab kb} a[m, k] * b[n, k] ) * sa[m, kb] * sb[n // 128, kb]
+
+This is the plain definition of a block-dequantised matmul.  The pages reach
+it through FP8 tensor-core sums per block followed by a higher-precision
+second accumulation level ("DeepSeek open-source week day 3",
+deepseek.csdn.net, "technical features", the two-level accumulation item);
+the oracle writes the definition out directly, slab by slab:
+
+* the per-slab dot products are taken in fp64 through a BLAS matmul.  They
+  are exact in any summation order: each product of two e4m3 values is an
+  integer multiple of 2^-18 below 2^17.6 in magnitude, so a 128-term sum
+  stays far inside the 53-bit fp64 significand;
+* the scale product sa * sb of two fp32 numbers is exact in fp64;
+* one rounding happens per slab when the scaled slab sum is added.
+
+So the result is the exact real-valued product to about (K/128) * 2^-53
+relative, far below the bf16 output precision.
+
+The grouped layouts follow the same page (MoE items):
+
+* contiguous: the rows of all experts are stacked in one M x K matrix and
+  each row carries an int32 expert index; row r uses expert m_indices[r]'s
+  B.  An index outside [0, G) marks a padding row, which has no result.
+* masked: A is G x max_m x K; expert g has masked_m[g] valid rows
+  (clamped to [0, max_m]); rows at or past that count have no result.
+
+Invalid entries are returned as NaN together with a boolean validity mask.
+"""
+
+import numpy as np
+
+from .e4m3 import decode_table
+
+SLAB = 128
+
+
+def _shapes(qa, sfa, qb, sfb):
+    m, k = qa.shape
+    n, k2 = qb.shape
+    if k != k2 or k % SLAB:
+        raise ValueError("A and B must share K, a multiple of 128")
+    kb = k // SLAB
+    nb = (n + SLAB - 1) // SLAB
+    if sfa.shape != (m, kb) or sfb.shape != (nb, kb):
+        raise ValueError(f"bad scale shapes {sfa.shape}, {sfb.shape}")
+    return m, n, k, kb
+
+
+def gemm_nt_ref(qa, sfa, qb, sfb):
+    """Dense reference.  qa: M x K codes, sfa: M x K/128, qb: N x K codes,
+    sfb: ceil(N/128) x K/128.  Returns the M x N fp64 result."""
+    qa = np.asarray(qa, np.uint8)
+    qb = np.asarray(qb, np.uint8)
+    m, n, k, kb = _shapes(qa, sfa, qb, sfb)
+    t = decode_table()
+    sa = np.asarray(sfa, np.float64)
+    sb = np.asarray(sfb, np.float64)
+    block_of_col = np.arange(n) // SLAB
+    r = np.zeros((m, n), dtype=np.float64)
+    for s in range(kb):
+        cols = slice(s * SLAB, (s + 1) * SLAB)
+        a_dec = t[qa[:, cols]]
+        b_dec = t[qb[:, cols]]
+        p = a_dec @ b_dec.T  # exact slab sums
+        scale = sa[:, s][:, None] * sb[block_of_col, s][None, :]
+        r += p * scale
+    return r
+
+
+def _entries(a_codes, sa_rows, b_codes, sb_rows):
+    """Element-wise results for paired rows: entry i is the dot of A row i
+    with B row i under their slab scales (same slab order as gemm_nt_ref)."""
+    t = decode_table()
+    s_cnt, k = a_codes.shape
+    kb = k // SLAB
+    out = np.zeros(s_cnt, dtype=np.float64)
+    chunk = max(1, (1 << 24) // max(k, 1))
+    for c0 in range(0, s_cnt, chunk):
+        c1 = min(s_cnt, c0 + chunk)
+        prod = t[a_codes[c0:c1]] * t[b_codes[c0:c1]]
+        p = prod.reshape(c1 - c0, kb, SLAB).sum(axis=2)  # exact slab sums
+        acc = np.zeros(c1 - c0, dtype=np.float64)
+        for s in range(kb):
+            acc += p[:, s] * (np.float64(1) * sa_rows[c0:c1, s] * sb_rows[c0:c1, s])
+        out[c0:c1] = acc
+    return out
+
+
+def gemm_nt_ref_at(qa, sfa, qb, sfb, rows, cols):
+    """Dense reference at the given (rows[i], cols[i]) output positions."""
+    rows = np.asarray(rows, np.int64)
+    cols = np.asarray(cols, np.int64)
+    sa = np.asarray(sfa, np.float64)
+    sb = np.asarray(sfb, np.float64)
+    return _entries(np.asarray(qa)[rows], sa[rows], np.asarray(qb)[cols], sb[cols // SLAB])
+
+
+def grouped_contiguous_ref(qa, sfa, qb, sfb, m_indices):
+    """Contiguous-layout grouped reference.
+
+    qa: M x K, sfa: M x K/128, qb: G x N x K, sfb: G x ceil(N/128) x K/128,
+    m_indices: M int32.  Returns (r, valid): r is M x N fp64 with NaN in
+    rows whose index is outside [0, G); valid is the M-long row mask.
+    """
+    g_cnt, n, _ = qb.shape
+    idx = np.asarray(m_indices, np.int64)
+    m = qa.shape[0]
+    r = np.full((m, n), np.nan, dtype=np.float64)
+    valid = (idx >= 0) & (idx < g_cnt)
+    for g in range(g_cnt):
+        rows = np.nonzero(idx == g)[0]
+        if rows.size:
+            r[rows] = gemm_nt_ref(qa[rows], sfa[rows], qb[g], sfb[g])
+    return r, valid
+
+
+def grouped_contiguous_ref_at(qa, sfa, qb, sfb, m_indices, rows, cols):
+    """Contiguous grouped reference at (rows[i], cols[i]); NaN where the row
+    is a padding row."""
+    g_cnt = qb.shape[0]
+    rows = np.asarray(rows, np.int64)
+    cols = np.asarray(cols, np.int64)
+    g = np.asarray(m_indices, np.int64)[rows]
+    ok = (g >= 0) & (g < g_cnt)
+    out = np.full(rows.shape, np.nan)
+    if ok.any():
+        rr, cc, gg = rows[ok], cols[ok], g[ok]
+        sa = np.asarray(sfa, np.float64)
+        sb = np.asarray(sfb, np.float64)
+        out[ok] = _entries(qa[rr], sa[rr], qb[gg, cc], sb[gg, cc // SLAB])
+    return out
+
+
+def _masked_counts(masked_m, max_m):
+    return np.clip(np.asarray(masked_m, np.int64), 0, max_m)
+
+
+def grouped_masked_ref(qa, sfa, qb, sfb, masked_m):
+    """Masked-layout grouped reference.
+
+    qa: G x max_m x K, sfa: G x max_m x K/128, qb: G x N x K,
+    sfb: G x ceil(N/128) x K/128, masked_m: G int32.  Returns (r, valid):
+    r is G x max_m x N fp64 with NaN in rows at or past min(masked_m[g], max_m).
+    """
+    g_cnt, max_m, _ = qa.shape
+    n = qb.shape[1]
+    cnt = _masked_counts(masked_m, max_m)
+    r = np.full((g_cnt, max_m, n), np.nan, dtype=np.float64)
+    valid = np.arange(max_m)[None, :] < cnt[:, None]
+    for g in range(g_cnt):
+        c = int(cnt[g])
+        if c:
+            r[g, :c] = gemm_nt_ref(qa[g, :c], sfa[g, :c], qb[g], sfb[g])
+    return r, valid
+
+
+def grouped_masked_ref_at(qa, sfa, qb, sfb, masked_m, groups, rows, cols):
+    """Masked grouped reference at (groups[i], rows[i], cols[i]); NaN where
+    the row is past the expert's valid count."""
+    g_cnt, max_m, _ = qa.shape
+    cnt = _masked_counts(masked_m, max_m)
+    groups = np.asarray(groups, np.int64)
+    rows = np.asarray(rows, np.int64)
+    cols = np.asarray(cols, np.int64)
+    ok = rows < cnt[groups]
+    out = np.full(rows.shape, np.nan)
+    if ok.any():
+        gg, rr, cc = groups[ok], rows[ok], cols[ok]
+        sa = np.asarray(sfa, np.float64)
+        sb = np.asarray(sfb, np.float64)
+        out[ok] = _entries(qa[gg, rr], sa[gg, rr], qb[gg, cc], sb[gg, cc // SLAB])
+    return out

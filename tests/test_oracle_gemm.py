@@ -1,0 +1,228 @@
+"""Pins for the oracle GEMMs.
+
+* exact-rational brute force on tiny shapes (fractions.Fraction, codes
+  decoded by torch's float8_e4m3fn conversion, not by the oracle's table);
+* with unit scales the result equals a plain whole-K matmul bit for bit;
+* closed forms: all-ones operands give K, per-slab and per-block scales give
+  128 * sum_kb sa[m,kb] * sb[n//128,kb];
+* invariants: scaling a row of sa scales that row of the result exactly,
+  the _at variants agree with the full ones bit for bit;
+* grouped layouts against the brute force: each row uses its own expert's B,
+  padding rows and rows past masked_m have no result, masked_m is clamped.
+"""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import (gemm_nt_ref, gemm_nt_ref_at, grouped_contiguous_ref,
+                    grouped_masked_ref, tolerance_check)
+from oracle.gemm import grouped_contiguous_ref_at, grouped_masked_ref_at
+
+SPECIAL = np.array([0x7E, 0xFE, 0x01, 0x81, 0x00, 0x80, 0x07, 0x08, 0x38, 0x5F], dtype=np.uint8)
+
+
+def lib_decode(codes):
+    t = torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def random_codes(rng, shape):
+    c = rng.integers(0, 256, size=shape).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x3F  # no NaN codes in operands
+    flat = c.reshape(-1)
+    pick = rng.random(flat.size) < 0.2
+    flat[pick] = rng.choice(SPECIAL, pick.sum())
+    return c
+
+
+def random_scales(rng, shape):
+    return (np.exp2(rng.uniform(-12, 2, shape)) * rng.uniform(1, 2, shape)).astype(np.float32)
+
+
+def brute(qa, sa, qb, sb):
+    """Exact rational result and the sum of |terms| per entry."""
+    m, k = qa.shape
+    n = qb.shape[0]
+    da, db = lib_decode(qa), lib_decode(qb)
+    r = np.zeros((m, n), dtype=object)
+    mag = np.zeros((m, n))
+    for i in range(m):
+        for j in range(n):
+            tot = Fraction(0)
+            ab = 0.0
+            for kb in range(k // 128):
+                sl = 0
+                for kk in range(kb * 128, (kb + 1) * 128):
+                    sl += Fraction(da[i, kk]) * Fraction(db[j, kk])
+                term = sl * Fraction(float(sa[i, kb])) * Fraction(float(sb[j // 128, kb]))
+                tot += term
+                ab += abs(float(term))
+            r[i, j] = tot
+            mag[i, j] = ab
+    return r, mag
+
+
+def assert_close_to_exact(got, exact, mag, kslabs):
+    bound = (kslabs + 1) * 2.0 ** -53 * mag
+    for idx in np.ndindex(got.shape):
+        assert abs(Fraction(float(got[idx])) - exact[idx]) <= Fraction(float(bound[idx])) + 0, idx
+
+
+@pytest.mark.parametrize("m,n,k", [(3, 5, 128), (5, 2, 256), (4, 4, 384), (1, 3, 256)])
+def test_dense_brute_force(m, n, k):
+    rng = np.random.default_rng(m * 100 + n * 10 + k)
+    qa, qb = random_codes(rng, (m, k)), random_codes(rng, (n, k))
+    sa, sb = random_scales(rng, (m, k // 128)), random_scales(rng, (1, k // 128))
+    exact, mag = brute(qa, sa, qb, sb)
+    assert_close_to_exact(gemm_nt_ref(qa, sa, qb, sb), exact, mag, k // 128)
+
+
+def test_dense_brute_force_two_b_blocks():
+    # N spans two 128-row scale blocks (the second partial): column n must use sb[n // 128]
+    rng = np.random.default_rng(11)
+    m, n, k = 2, 131, 256
+    qa, qb = random_codes(rng, (m, k)), random_codes(rng, (n, k))
+    sa, sb = random_scales(rng, (m, 2)), random_scales(rng, (2, 2))
+    cols = [0, 1, 127, 128, 130]
+    got = gemm_nt_ref(qa, sa, qb, sb)[:, cols]
+    da, db = lib_decode(qa), lib_decode(qb)
+    for i in range(m):
+        for jj, j in enumerate(cols):
+            tot, ab = Fraction(0), 0.0
+            for kb in range(2):
+                sl = sum(Fraction(da[i, kk]) * Fraction(db[j, kk]) for kk in range(kb * 128, kb * 128 + 128))
+                term = sl * Fraction(float(sa[i, kb])) * Fraction(float(sb[j // 128, kb]))
+                tot += term
+                ab += abs(float(term))
+            assert abs(Fraction(float(got[i, jj])) - tot) <= Fraction(3 * 2.0 ** -53 * ab)
+
+
+def test_unit_scales_equal_plain_matmul_bitwise():
+    rng = np.random.default_rng(3)
+    m, n, k = 33, 70, 1024
+    qa, qb = random_codes(rng, (m, k)), random_codes(rng, (n, k))
+    r = gemm_nt_ref(qa, np.ones((m, 8), np.float32), qb, np.ones((1, 8), np.float32))
+    ref = torch.from_numpy(lib_decode(qa)) @ torch.from_numpy(lib_decode(qb)).T
+    assert np.array_equal(r, ref.numpy())
+
+
+def test_ones_closed_forms():
+    m, n, k = 4, 320, 1024
+    qa = np.full((m, k), 0x38, np.uint8)  # 1.0
+    qb = np.full((n, k), 0x38, np.uint8)
+    r = gemm_nt_ref(qa, np.ones((m, 8), np.float32), qb, np.ones((3, 8), np.float32))
+    assert np.all(r == k)
+    r = gemm_nt_ref(qa, np.full((m, 8), 0.5, np.float32), qb, np.full((3, 8), 3.0, np.float32))
+    assert np.all(r == 1.5 * k)
+    rng = np.random.default_rng(4)
+    sa, sb = random_scales(rng, (m, 8)), random_scales(rng, (3, 8))
+    r = gemm_nt_ref(qa, sa, qb, sb)
+    expect = 128.0 * np.einsum("mk,bk->mb", sa.astype(np.float64), sb.astype(np.float64))
+    np.testing.assert_allclose(r, expect[:, np.arange(n) // 128], rtol=1e-15)
+
+
+def test_row_scale_linearity_exact():
+    rng = np.random.default_rng(9)
+    m, n, k = 6, 40, 512
+    qa, qb = random_codes(rng, (m, k)), random_codes(rng, (n, k))
+    sa, sb = random_scales(rng, (m, 4)), random_scales(rng, (1, 4))
+    r1 = gemm_nt_ref(qa, sa, qb, sb)
+    sa2 = sa.copy()
+    sa2[2] *= 2
+    r2 = gemm_nt_ref(qa, sa2, qb, sb)
+    assert np.array_equal(r2[2], 2 * r1[2])
+    assert np.array_equal(np.delete(r2, 2, 0), np.delete(r1, 2, 0))
+
+
+def test_at_variant_matches_full_bitwise():
+    rng = np.random.default_rng(10)
+    m, n, k = 50, 300, 768
+    qa, qb = random_codes(rng, (m, k)), random_codes(rng, (n, k))
+    sa, sb = random_scales(rng, (m, 6)), random_scales(rng, (3, 6))
+    full = gemm_nt_ref(qa, sa, qb, sb)
+    rows = rng.integers(0, m, 500)
+    cols = rng.integers(0, n, 500)
+    assert np.array_equal(gemm_nt_ref_at(qa, sa, qb, sb, rows, cols), full[rows, cols])
+
+
+def test_contiguous_against_brute_force():
+    rng = np.random.default_rng(12)
+    g, m, n, k = 3, 7, 4, 256
+    qa = random_codes(rng, (m, k))
+    sa = random_scales(rng, (m, 2))
+    qb = random_codes(rng, (g, n, k))
+    sb = random_scales(rng, (g, 1, 2))
+    idx = np.array([2, 0, -1, 1, 2, 5, 0], dtype=np.int32)  # -1 and 5: no result
+    r, valid = grouped_contiguous_ref(qa, sa, qb, sb, idx)
+    assert list(valid) == [True, True, False, True, True, False, True]
+    assert np.all(np.isnan(r[~valid]))
+    for row in np.nonzero(valid)[0]:
+        e = idx[row]
+        exact, mag = brute(qa[row:row + 1], sa[row:row + 1], qb[e], sb[e])
+        assert_close_to_exact(r[row:row + 1], exact, mag, 2)
+    rows = np.array([0, 2, 3, 5, 6, 6])
+    cols = np.array([1, 0, 3, 2, 0, 3])
+    at = grouped_contiguous_ref_at(qa, sa, qb, sb, idx, rows, cols)
+    assert np.array_equal(np.isnan(at), np.isnan(r[rows, cols]))
+    ok = ~np.isnan(at)
+    assert np.array_equal(at[ok], r[rows, cols][ok])
+
+
+def test_contiguous_equals_per_group_dense():
+    rng = np.random.default_rng(13)
+    g, n, k = 4, 64, 384
+    idx = np.repeat(np.arange(g, dtype=np.int32), [5, 0, 9, 3])
+    m = idx.size
+    qa, sa = random_codes(rng, (m, k)), random_scales(rng, (m, 3))
+    qb, sb = random_codes(rng, (g, n, k)), random_scales(rng, (g, 1, 3))
+    r, valid = grouped_contiguous_ref(qa, sa, qb, sb, idx)
+    assert valid.all()
+    for e in range(g):
+        rows = idx == e
+        if rows.any():
+            # a different, independent route: the dense oracle on that expert's rows
+            # against brute force on one sampled row
+            i = np.nonzero(rows)[0][0]
+            exact, mag = brute(qa[i:i + 1], sa[i:i + 1], qb[e][:3], sb[e])
+            assert_close_to_exact(r[i:i + 1, :3], exact, mag, 3)
+
+
+def test_masked_against_brute_force_and_clamping():
+    rng = np.random.default_rng(14)
+    g, max_m, n, k = 4, 5, 3, 256
+    qa, sa = random_codes(rng, (g, max_m, k)), random_scales(rng, (g, max_m, 2))
+    qb, sb = random_codes(rng, (g, n, k)), random_scales(rng, (g, 1, 2))
+    masked_m = np.array([2, 0, 9, -3], dtype=np.int32)  # 9 clamps to 5, -3 to 0
+    r, valid = grouped_masked_ref(qa, sa, qb, sb, masked_m)
+    assert valid.sum(axis=1).tolist() == [2, 0, 5, 0]
+    assert np.all(np.isnan(r[~valid])) and not np.any(np.isnan(r[valid]))
+    for e, cnt in [(0, 2), (2, 5)]:
+        exact, mag = brute(qa[e, :cnt], sa[e, :cnt], qb[e], sb[e])
+        assert_close_to_exact(r[e, :cnt], exact, mag, 2)
+    gs = np.array([0, 0, 1, 2, 2, 3])
+    rs = np.array([1, 2, 0, 4, 0, 0])
+    cs = np.array([0, 1, 2, 2, 1, 0])
+    at = grouped_masked_ref_at(qa, sa, qb, sb, masked_m, gs, rs, cs)
+    full = r[gs, rs, cs]
+    assert np.array_equal(np.isnan(at), np.isnan(full))
+    assert np.array_equal(at[~np.isnan(at)], full[~np.isnan(full)])
+
+
+def test_tolerance_rule():
+    r = np.array([1.0, -2.0, 1e-6, 100.0])
+    rms = float(np.sqrt(np.mean(r * r)))
+    assert tolerance_check(r.copy(), r)["ok"]
+    d = r * (1 + 7e-3)
+    assert tolerance_check(d, r)["ok"]
+    d = r.copy()
+    d[1] *= 1.05  # err 0.1 > 8e-3*2 + 1e-3*rms (rms ~ 50)
+    assert not tolerance_check(d, r)["ok"]
+    d = r.copy()
+    d[2] = 1e-3 * rms * 0.9  # near-zero element: absolute term covers it
+    assert tolerance_check(d, r)["ok"]
+    d[2] = np.nan
+    res = tolerance_check(d, r)
+    assert not res["ok"] and res["n_bad"] == 1
