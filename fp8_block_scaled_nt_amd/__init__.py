@@ -1,0 +1,223 @@
+"""Python binding of the gfx950 FP8 block-scaled NT GEMM library (libdg.so).
+
+The binding only marshals arguments: it checks dtypes, shapes and devices of
+torch tensors, passes their device pointers and the current HIP stream to the
+C ABI (include/dg.h), and raises on a non-zero status.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback.  PyTorch
+supplies device memory and streams.
+
+Layouts (all row-major, packed):
+  a    [m, k] e4m3 codes (torch.float8_e4m3fn or uint8); masked: [g, max_m, k]
+  sfa  slab-major fp32 [k/128, get_sfa_ld(m)]; masked: [g, k/128, get_sfa_ld(max_m)]
+  b    [n, k] e4m3; grouped: [g, n, k]
+  sfb  fp32 [ceil(n/128), k/128]; grouped: [g, ceil(n/128), k/128]
+  d    bf16 [m, n]; masked: [g, max_m, n]
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libdg.so")
+
+__all__ = [
+    "DGError", "lib", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous",
+    "m_grouped_fp8_gemm_nt_masked", "quantize_a_1x128", "quantize_b_128x128",
+    "get_m_alignment_for_contiguous_layout", "get_sfa_ld", "empty_sfa",
+]
+
+
+class DGError(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, status, message):
+        super().__init__(f"dg status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+_vp, _ci = ctypes.c_void_p, ctypes.c_int
+_SIGNATURES = {
+    "dg_fp8_gemm_nt": [_vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _vp],
+    "dg_m_grouped_fp8_gemm_nt_contiguous": [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _vp],
+    "dg_m_grouped_fp8_gemm_nt_masked": [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _vp],
+    "dg_get_m_alignment_for_contiguous_layout": [],
+    "dg_get_sfa_ld": [_ci],
+    "dg_quantize_a_1x128": [_vp, _vp, _vp, _ci, _ci, _vp],
+    "dg_quantize_b_128x128": [_vp, _vp, _vp, _ci, _ci, _vp],
+    "dg_status_string": [_ci],
+    "dg_last_error_message": [],
+    "dg_version": [],
+}
+_RESTYPES = {"dg_status_string": ctypes.c_char_p, "dg_last_error_message": ctypes.c_char_p,
+             "dg_version": ctypes.c_char_p}
+
+
+def lib():
+    """Load libdg.so (built in-tree by build.py); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run fp8_block_scaled_nt_amd/build.py")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGNATURES.items():
+            f = getattr(h, name)
+            f.argtypes = args
+            f.restype = _RESTYPES.get(name, ctypes.c_int)
+        _lib = h
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        msg = lib().dg_last_error_message().decode()
+        raise DGError(status, msg or lib().dg_status_string(status).decode())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+_FP8 = (torch.float8_e4m3fn, torch.uint8)
+
+
+def _need(t, name, dtypes, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def get_m_alignment_for_contiguous_layout():
+    return lib().dg_get_m_alignment_for_contiguous_layout()
+
+
+def get_sfa_ld(m):
+    return lib().dg_get_sfa_ld(int(m))
+
+
+def empty_sfa(m, k, groups=None, device="cuda"):
+    """Allocate a slab-major sfa buffer for m rows (optionally per group)."""
+    shape = (k // 128, get_sfa_ld(m))
+    if groups is not None:
+        shape = (groups,) + shape
+    return torch.empty(shape, dtype=torch.float32, device=device)
+
+
+def fp8_gemm_nt(a_pair, b_pair, d):
+    """D = A . B^T with block scales.  a_pair = (a [m,k], sfa), b_pair = (b [n,k], sfb),
+    d: bf16 [m, n], written in place."""
+    a, sfa = a_pair
+    b, sfb = b_pair
+    _need(a, "a", _FP8, 2)
+    _need(b, "b", _FP8, 2)
+    _need(d, "d", (torch.bfloat16,), 2)
+    _need(sfa, "sfa", (torch.float32,), 2)
+    _need(sfb, "sfb", (torch.float32,), 2)
+    m, k = a.shape
+    n = b.shape[0]
+    if b.shape[1] != k or tuple(d.shape) != (m, n):
+        raise ValueError(f"shape mismatch a{tuple(a.shape)} b{tuple(b.shape)} d{tuple(d.shape)}")
+    if tuple(sfa.shape) != (k // 128, get_sfa_ld(m)):
+        raise ValueError(f"sfa must be [k/128, sfa_ld(m)] = {(k // 128, get_sfa_ld(m))}")
+    if tuple(sfb.shape) != ((n + 127) // 128, k // 128):
+        raise ValueError("sfb must be [ceil(n/128), k/128]")
+    _check(lib().dg_fp8_gemm_nt(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(d), m, n, k, _stream()))
+    return d
+
+
+def m_grouped_fp8_gemm_nt_contiguous(a_pair, b_pair, d, m_indices):
+    """Contiguous-layout grouped GEMM: row r of a uses expert m_indices[r]'s B."""
+    a, sfa = a_pair
+    b, sfb = b_pair
+    _need(a, "a", _FP8, 2)
+    _need(b, "b", _FP8, 3)
+    _need(d, "d", (torch.bfloat16,), 2)
+    _need(sfa, "sfa", (torch.float32,), 2)
+    _need(sfb, "sfb", (torch.float32,), 3)
+    _need(m_indices, "m_indices", (torch.int32,), 1)
+    m, k = a.shape
+    g, n, _ = b.shape
+    if b.shape[2] != k or tuple(d.shape) != (m, n) or m_indices.numel() != m:
+        raise ValueError("shape mismatch")
+    if tuple(sfa.shape) != (k // 128, get_sfa_ld(m)) or tuple(sfb.shape) != (g, (n + 127) // 128, k // 128):
+        raise ValueError("scale shape mismatch")
+    _check(lib().dg_m_grouped_fp8_gemm_nt_contiguous(
+        _ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(d), _ptr(m_indices), m, n, k, g, _stream()))
+    return d
+
+
+def m_grouped_fp8_gemm_nt_masked(a_pair, b_pair, d, masked_m, expected_m=0):
+    """Masked-layout grouped GEMM: expert g computes its first masked_m[g] rows."""
+    a, sfa = a_pair
+    b, sfb = b_pair
+    _need(a, "a", _FP8, 3)
+    _need(b, "b", _FP8, 3)
+    _need(d, "d", (torch.bfloat16,), 3)
+    _need(sfa, "sfa", (torch.float32,), 3)
+    _need(sfb, "sfb", (torch.float32,), 3)
+    _need(masked_m, "masked_m", (torch.int32,), 1)
+    g, max_m, k = a.shape
+    n = b.shape[1]
+    if b.shape[0] != g or b.shape[2] != k or tuple(d.shape) != (g, max_m, n) or masked_m.numel() != g:
+        raise ValueError("shape mismatch")
+    if tuple(sfa.shape) != (g, k // 128, get_sfa_ld(max_m)) or tuple(sfb.shape) != (g, (n + 127) // 128, k // 128):
+        raise ValueError("scale shape mismatch")
+    _check(lib().dg_m_grouped_fp8_gemm_nt_masked(
+        _ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(d), _ptr(masked_m), g, max_m, n, k,
+        int(expected_m), _stream()))
+    return d
+
+
+def quantize_a_1x128(x, q=None, sfa=None):
+    """fp32 [m, k] (or [g, m, k]) -> (e4m3 codes, slab-major sfa)."""
+    _need(x, "x", (torch.float32,), x.dim())
+    if x.dim() == 3:
+        g, m, k = x.shape
+        q = torch.empty((g, m, k), dtype=torch.float8_e4m3fn, device=x.device) if q is None else q
+        sfa = empty_sfa(m, k, g, x.device) if sfa is None else sfa
+        for i in range(g):
+            quantize_a_1x128(x[i], q[i], sfa[i])
+        return q, sfa
+    m, k = x.shape
+    q = torch.empty((m, k), dtype=torch.float8_e4m3fn, device=x.device) if q is None else q
+    sfa = empty_sfa(m, k, None, x.device) if sfa is None else sfa
+    _need(q, "q", _FP8, 2)
+    _need(sfa, "sfa", (torch.float32,), 2)
+    if tuple(q.shape) != (m, k) or tuple(sfa.shape) != (k // 128, get_sfa_ld(m)):
+        raise ValueError("output shape mismatch")
+    _check(lib().dg_quantize_a_1x128(_ptr(x), _ptr(q), _ptr(sfa), m, k, _stream()))
+    return q, sfa
+
+
+def quantize_b_128x128(x, q=None, sfb=None):
+    """fp32 [n, k] (or [g, n, k]) -> (e4m3 codes, sfb [.., ceil(n/128), k/128])."""
+    _need(x, "x", (torch.float32,), x.dim())
+    if x.dim() == 3:
+        g, n, k = x.shape
+        q = torch.empty((g, n, k), dtype=torch.float8_e4m3fn, device=x.device) if q is None else q
+        sfb = torch.empty((g, (n + 127) // 128, k // 128), dtype=torch.float32, device=x.device) if sfb is None else sfb
+        for i in range(g):
+            quantize_b_128x128(x[i], q[i], sfb[i])
+        return q, sfb
+    n, k = x.shape
+    q = torch.empty((n, k), dtype=torch.float8_e4m3fn, device=x.device) if q is None else q
+    sfb = torch.empty(((n + 127) // 128, k // 128), dtype=torch.float32, device=x.device) if sfb is None else sfb
+    _need(q, "q", _FP8, 2)
+    _need(sfb, "sfb", (torch.float32,), 2)
+    if tuple(q.shape) != (n, k) or tuple(sfb.shape) != ((n + 127) // 128, k // 128):
+        raise ValueError("output shape mismatch")
+    _check(lib().dg_quantize_b_128x128(_ptr(x), _ptr(q), _ptr(sfb), n, k, _stream()))
+    return q, sfb

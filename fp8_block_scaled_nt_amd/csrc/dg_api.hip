@@ -1,0 +1,323 @@
+// C ABI of the FP8 block-scaled NT GEMM library (declared in include/dg.h):
+// argument validation, per-shape choice among the compile-time tile
+// configurations, and the kernel launches.  The pages' DeepGEMM compiles a
+// kernel per shape at run time ("DeepSeek open-source week day 3",
+// technical features, JIT item); here every configuration is compiled ahead
+// of time for gfx950 and the host picks one per call from (M, N, K, groups,
+// CU count), which keeps the call free of compilation, allocation and
+// synchronisation.
+#include "../../include/dg.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "gemm_kernel.h"
+#include "quant_kernel.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return DG_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int sfa_ld(int m) { return (m + 3) / 4 * 4; }
+
+bool log_enabled() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("DG_LOG");
+    v = (e && *e && *e != '0') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+// ---- per-device facts, queried once per device
+struct DeviceInfo {
+  int cus = 0;
+  bool ok = false;
+};
+constexpr int kMaxDevices = 64;
+DeviceInfo g_dev[kMaxDevices];
+std::once_flag g_dev_once[kMaxDevices];
+
+int current_device(int* dev, DeviceInfo** info) {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+    (void)hipGetLastError();
+    return fail(DG_ERR_NO_DEVICE, "no HIP device is visible");
+  }
+  if (hipGetDevice(dev) != hipSuccess || *dev < 0 || *dev >= kMaxDevices)
+    return fail(DG_ERR_NO_DEVICE, "hipGetDevice failed");
+  const int d = *dev;
+  std::call_once(g_dev_once[d], [d]() {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, d) != hipSuccess) return;
+    g_dev[d].cus = prop.multiProcessorCount;
+    g_dev[d].ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  });
+  if (!g_dev[d].ok) return fail(DG_ERR_NO_DEVICE, "device %d is not a gfx950 GPU", d);
+  *info = &g_dev[d];
+  return DG_OK;
+}
+
+// ---- tile configurations
+struct Config {
+  const char* name;
+  int variant, bm, bn, wm, wn;
+  const void* fn;
+  int smem;
+  int threads() const { return wm * wn * 64; }
+};
+
+template <int BM, int BN, int WM, int WN, int VAR>
+Config make_config(const char* name) {
+  return Config{name, VAR, BM, BN, WM, WN,
+                reinterpret_cast<const void*>(&dg::gemm_fp8_nt_kernel<BM, BN, WM, WN, VAR>),
+                dg::Smem<BM, BN>::kBytes};
+}
+
+const Config* configs(int* count) {
+  static const Config table[] = {
+      // dense
+      make_config<256, 256, 2, 4, dg::kDense>("dense_256x256_w8"),
+      make_config<128, 128, 2, 2, dg::kDense>("dense_128x128_w4"),
+      make_config<64, 64, 1, 4, dg::kDense>("dense_64x64_w4"),
+      // contiguous (block rows <= the 128-row alignment)
+      make_config<128, 256, 2, 4, dg::kContiguous>("contig_128x256_w8"),
+      make_config<128, 128, 2, 2, dg::kContiguous>("contig_128x128_w4"),
+      // masked
+      make_config<256, 128, 1, 4, dg::kMasked>("masked_256x128_w4"),
+      make_config<64, 64, 1, 4, dg::kMasked>("masked_64x64_w4"),
+  };
+  *count = sizeof(table) / sizeof(table[0]);
+  return table;
+}
+
+const Config* find_config(const char* name, int variant) {
+  int cnt = 0;
+  const Config* t = configs(&cnt);
+  for (int i = 0; i < cnt; ++i)
+    if (t[i].variant == variant && strcmp(t[i].name, name) == 0) return &t[i];
+  return nullptr;
+}
+
+const Config* forced_config(int variant) {
+  const char* e = getenv("DG_FORCE_CONFIG");
+  if (!e || !*e) return nullptr;
+  return find_config(e, variant);
+}
+
+std::once_flag g_attr_once;
+hipError_t g_attr_err = hipSuccess;
+
+void set_kernel_attributes() {
+  int cnt = 0;
+  const Config* t = configs(&cnt);
+  for (int i = 0; i < cnt; ++i) {
+    hipError_t e = hipFuncSetAttribute(t[i].fn, hipFuncAttributeMaxDynamicSharedMemorySize, t[i].smem);
+    if (e != hipSuccess) g_attr_err = e;
+  }
+}
+
+int launch(const Config& c, dg::GemmParams& p, int grid, hipStream_t stream) {
+  std::call_once(g_attr_once, set_kernel_attributes);
+  if (g_attr_err != hipSuccess)
+    return fail(DG_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(g_attr_err));
+  if (log_enabled())
+    fprintf(stderr, "[dg] %s m=%d n=%d k=%d groups=%d grid=%d threads=%d smem=%d\n", c.name, p.m, p.n,
+            p.k, p.num_groups, grid, c.threads(), c.smem);
+  if (grid <= 0) return ok();
+  void* args[] = {&p};
+  hipError_t e = hipLaunchKernel(c.fn, dim3(grid), dim3(c.threads()), args, c.smem, stream);
+  if (e != hipSuccess) return fail(DG_ERR_HIP, "launch of %s failed: %s", c.name, hipGetErrorString(e));
+  return ok();
+}
+
+void fill_common(dg::GemmParams& p, const Config& c, int m, int n, int k) {
+  p.m = m;
+  p.n = n;
+  p.k = k;
+  p.kb_count = k / 128;
+  p.nb_count = (n + 127) / 128;
+  p.sfa_ld = sfa_ld(m);
+  p.tiles_m = (m + c.bm - 1) / c.bm;
+  p.tiles_n = (n + c.bn - 1) / c.bn;
+  p.group_m = 8;
+}
+
+int check_k_n(int n, int k) {
+  if (n < 1) return fail(DG_ERR_INVALID_ARGUMENT, "n must be >= 1 (got %d)", n);
+  if (k < 128 || k % 128 != 0)
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "k must be a positive multiple of 128 (got %d)", k);
+  return DG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dg_get_m_alignment_for_contiguous_layout(void) { return 128; }
+
+int dg_get_sfa_ld(int m) { return m < 0 ? 0 : sfa_ld(m); }
+
+const char* dg_version(void) { return "dg-gfx950 0.1"; }
+
+const char* dg_status_string(int status) {
+  switch (status) {
+    case DG_OK: return "ok";
+    case DG_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case DG_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case DG_ERR_MISALIGNED: return "misaligned pointer";
+    case DG_ERR_NO_DEVICE: return "no usable gfx950 device";
+    case DG_ERR_HIP: return "HIP runtime error";
+    case DG_ERR_INTERNAL: return "internal error";
+    default: return "unknown status";
+  }
+}
+
+const char* dg_last_error_message(void) { return g_last_error.c_str(); }
+
+int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb, uint16_t* d,
+                   int m, int n, int k, dg_stream_t stream) {
+  if (!a || !sfa || !b || !sfb || !d) return fail(DG_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (m < 0) return fail(DG_ERR_INVALID_ARGUMENT, "m must be >= 0 (got %d)", m);
+  if (int s = check_k_n(n, k)) return s;
+  if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d))
+    return fail(DG_ERR_MISALIGNED, "pointers must be 16-byte aligned");
+  if (m == 0) return ok();
+  int dev;
+  DeviceInfo* info;
+  if (int s = current_device(&dev, &info)) return s;
+  const Config* c = forced_config(dg::kDense);
+  if (!c) {
+    if (m <= 64) c = find_config("dense_64x64_w4", dg::kDense);
+    else if (m <= 256 || n <= 256) c = find_config("dense_128x128_w4", dg::kDense);
+    else c = find_config("dense_256x256_w8", dg::kDense);
+  }
+  dg::GemmParams p{};
+  p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d;
+  p.num_groups = 1;
+  fill_common(p, *c, m, n, k);
+  p.num_tiles = p.tiles_m * p.tiles_n;
+  return launch(*c, p, p.num_tiles, (hipStream_t)stream);
+}
+
+int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b,
+                                        const float* sfb, uint16_t* d, const int32_t* m_indices, int m,
+                                        int n, int k, int num_groups, dg_stream_t stream) {
+  if (!a || !sfa || !b || !sfb || !d || !m_indices)
+    return fail(DG_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (m < 0) return fail(DG_ERR_INVALID_ARGUMENT, "m must be >= 0 (got %d)", m);
+  if (num_groups < 1) return fail(DG_ERR_INVALID_ARGUMENT, "num_groups must be >= 1 (got %d)", num_groups);
+  if (int s = check_k_n(n, k)) return s;
+  if (m % 128 != 0)
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "m must be a multiple of the 128-row alignment (got %d)", m);
+  if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d) ||
+      (reinterpret_cast<uintptr_t>(m_indices) & 3u))
+    return fail(DG_ERR_MISALIGNED, "pointers must be 16-byte aligned (m_indices 4-byte)");
+  if (m == 0) return ok();
+  int dev;
+  DeviceInfo* info;
+  if (int s = current_device(&dev, &info)) return s;
+  const Config* c = forced_config(dg::kContiguous);
+  if (!c) c = find_config(n >= 256 ? "contig_128x256_w8" : "contig_128x128_w4", dg::kContiguous);
+  dg::GemmParams p{};
+  p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.m_indices = m_indices;
+  p.num_groups = num_groups;
+  fill_common(p, *c, m, n, k);
+  p.num_tiles = p.tiles_m * p.tiles_n;
+  return launch(*c, p, p.num_tiles, (hipStream_t)stream);
+}
+
+int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const uint8_t* b,
+                                    const float* sfb, uint16_t* d, const int32_t* masked_m,
+                                    int num_groups, int max_m, int n, int k, int expected_m,
+                                    dg_stream_t stream) {
+  if (!a || !sfa || !b || !sfb || !d || !masked_m)
+    return fail(DG_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (num_groups < 0) return fail(DG_ERR_INVALID_ARGUMENT, "num_groups must be >= 0 (got %d)", num_groups);
+  if (max_m < 0) return fail(DG_ERR_INVALID_ARGUMENT, "max_m must be >= 0 (got %d)", max_m);
+  if (expected_m < 0) return fail(DG_ERR_INVALID_ARGUMENT, "expected_m must be >= 0 (got %d)", expected_m);
+  if (int s = check_k_n(n, k)) return s;
+  if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d) ||
+      (reinterpret_cast<uintptr_t>(masked_m) & 3u))
+    return fail(DG_ERR_MISALIGNED, "pointers must be 16-byte aligned (masked_m 4-byte)");
+  if (num_groups == 0 || max_m == 0) return ok();
+  int dev;
+  DeviceInfo* info;
+  if (int s = current_device(&dev, &info)) return s;
+  const Config* c = forced_config(dg::kMasked);
+  if (!c) c = find_config(max_m <= 64 ? "masked_64x64_w4" : "masked_256x128_w4", dg::kMasked);
+  dg::GemmParams p{};
+  p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.masked_m = masked_m;
+  p.num_groups = num_groups;
+  fill_common(p, *c, max_m, n, k);
+  p.num_tiles = num_groups * p.tiles_m * p.tiles_n;
+  return launch(*c, p, p.num_tiles, (hipStream_t)stream);
+}
+
+int dg_quantize_a_1x128(const float* x, uint8_t* q, float* sfa, int m, int k, dg_stream_t stream) {
+  if (!x || !q || !sfa) return fail(DG_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (m < 0) return fail(DG_ERR_INVALID_ARGUMENT, "m must be >= 0 (got %d)", m);
+  if (k < 128 || k % 128 != 0)
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "k must be a positive multiple of 128 (got %d)", k);
+  if (!aligned16(x) || !aligned16(q) || !aligned16(sfa))
+    return fail(DG_ERR_MISALIGNED, "pointers must be 16-byte aligned");
+  if (m == 0) return ok();
+  int dev;
+  DeviceInfo* info;
+  if (int s = current_device(&dev, &info)) return s;
+  const int ld = sfa_ld(m);
+  const long long units = (long long)ld * ((k / 128 + 1) / 2);
+  const long long grid = (units + 3) / 4;
+  if (grid > 0x7fffffffLL) return fail(DG_ERR_UNSUPPORTED_SHAPE, "matrix too large");
+  hipLaunchKernelGGL(dg::quant_a_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, x, q, sfa,
+                     m, k, ld);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DG_ERR_HIP, "quant_a launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int dg_quantize_b_128x128(const float* x, uint8_t* q, float* sfb, int n, int k, dg_stream_t stream) {
+  if (!x || !q || !sfb) return fail(DG_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (n < 0) return fail(DG_ERR_INVALID_ARGUMENT, "n must be >= 0 (got %d)", n);
+  if (k < 128 || k % 128 != 0)
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "k must be a positive multiple of 128 (got %d)", k);
+  if (!aligned16(x) || !aligned16(q) || !aligned16(sfb))
+    return fail(DG_ERR_MISALIGNED, "pointers must be 16-byte aligned");
+  if (n == 0) return ok();
+  int dev;
+  DeviceInfo* info;
+  if (int s = current_device(&dev, &info)) return s;
+  const long long grid = (long long)((n + 127) / 128) * (k / 128);
+  if (grid > 0x7fffffffLL) return fail(DG_ERR_UNSUPPORTED_SHAPE, "matrix too large");
+  hipLaunchKernelGGL(dg::quant_b_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, x, q, sfb,
+                     n, k);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DG_ERR_HIP, "quant_b launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,141 @@
+/*
+ * dg.h - C ABI of the MI355X (gfx950) FP8 block-scaled NT GEMM library.
+ *
+ * What the library computes (D = A . B^T with fine-grained scales):
+ *
+ *   D[m, n] = bf16( sum over 128-wide K slabs kb of
+ *                   (sum_{k in slab} A[m, k] * B[n, k]) * sfa[m, kb] * sfb[n / 128, kb] )
+ *
+ * A and B hold OCP e4m3 codes (1 byte, largest finite 448).  A carries one
+ * fp32 scale per row and 128-wide K slab; B one fp32 scale per 128 x 128
+ * block.  The operation and its MoE layouts are the ones described on the
+ * DeepGEMM pages: "DeepSeek open-source week day 3" (deepseek.csdn.net),
+ * section "technical features" (FP8 GEMM with fine-grained scaling and a
+ * second, higher-precision accumulation level; contiguous and masked grouped
+ * layouts); "DeepGEMM: making LLM matrix multiplication fly" (pomoai.com),
+ * sections "core functions" (block-wise scaling) and "technical details"
+ * (the fp8_gemm_nt naming: both operands K-contiguous).  The 1x128 / 128x128
+ * granularity, e4m3 and the bf16 output are readings of those pages.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer argument is caller-owned DEVICE memory (hipMalloc'd or a
+ *   torch CUDA tensor) on the current device.  The library never frees,
+ *   keeps or allocates anything on behalf of a call's arguments.
+ * - Every compute call is asynchronous on `stream` (0 = the null stream),
+ *   performs no host<->device copy, no synchronisation and no device memory
+ *   allocation, and reads no device value on the host.  The calls are
+ *   therefore capturable into a HIP graph.
+ * - Layouts are packed and row-major:
+ *     A       [m][k]               (masked: [num_groups][max_m][k])
+ *     B       [n][k]               (grouped: [num_groups][n][k])
+ *     D       [m][n] bf16 bits     (masked: [num_groups][max_m][n])
+ *     sfa     slab-major [k/128][ld], ld = dg_get_sfa_ld(m): sfa[kb*ld + row]
+ *             (masked: [num_groups][k/128][dg_get_sfa_ld(max_m)])
+ *     sfb     [ceil(n/128)][k/128] (grouped: [num_groups][ceil(n/128)][k/128])
+ * - Preconditions checked on the host: non-null pointers, A/B/D/sfa/sfb
+ *   16-byte aligned, k >= 128 and k % 128 == 0, n >= 1, m >= 0.  m == 0 (or
+ *   num_groups == 0 rows) is a successful no-op.  On a failed check nothing
+ *   is enqueued, D is untouched and a status other than DG_OK is returned;
+ *   dg_last_error_message() then describes the failure.
+ * - D is overwritten (not accumulated) for valid rows only; every other
+ *   element of D is left bit-for-bit untouched.
+ * - No exception crosses this interface.  All functions are thread-safe.
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* dg_stream_t; /* the same handle as hipStream_t */
+
+typedef enum {
+  DG_OK = 0,
+  DG_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, bad count        */
+  DG_ERR_UNSUPPORTED_SHAPE = 2, /* k not a multiple of 128, m not aligned, ...  */
+  DG_ERR_MISALIGNED = 3,        /* a pointer not 16-byte aligned                 */
+  DG_ERR_NO_DEVICE = 4,         /* no usable gfx950 device                       */
+  DG_ERR_HIP = 5,               /* a HIP runtime call or kernel launch failed     */
+  DG_ERR_INTERNAL = 6
+} dg_status;
+
+/*
+ * Dense FP8 NT GEMM: D[m][n] = A[m][k] . B[n][k]^T with 1x128 (A) and
+ * 128x128 (B) fp32 block scales.  Rows m and columns n may be any size >= 0
+ * and >= 1 respectively; a partial last 128-row block of B uses its own scale
+ * row of sfb.
+ */
+int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                   uint16_t* d, int m, int n, int k, dg_stream_t stream);
+
+/*
+ * MoE grouped GEMM, contiguous layout ("DeepSeek open-source week day 3",
+ * technical features, MoE item on the contiguous layout): the rows of all
+ * experts are stacked in A (m rows), experts share n and k, and
+ * m_indices[r] (device int32, m entries) names the expert whose B row r
+ * uses.  Each aligned block of dg_get_m_alignment_for_contiguous_layout()
+ * rows must belong to one expert; rows tagged outside [0, num_groups)
+ * (padding, conventionally -1) are neither computed nor written, nor are
+ * rows whose tag differs from the expert of their block.
+ * m must be a multiple of that alignment (else DG_ERR_UNSUPPORTED_SHAPE).
+ */
+int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b,
+                                        const float* sfb, uint16_t* d, const int32_t* m_indices,
+                                        int m, int n, int k, int num_groups, dg_stream_t stream);
+
+/*
+ * MoE grouped GEMM, masked layout ("DeepSeek open-source week day 3",
+ * technical features, MoE item on the masked layout; PPIO's evaluation,
+ * masked-layout section, decode use): every expert g owns a fixed
+ * max_m x k slab of A and max_m x n slab of D; masked_m[g] (device int32,
+ * num_groups entries, clamped on the device to [0, max_m]) says how many
+ * leading rows are valid.  Only valid rows are computed and written, so the
+ * shapes never change and the call suits graph capture.  expected_m is a
+ * host-side hint of the typical valid count (0 = unknown); it only steers
+ * the tile choice and never changes results.
+ */
+int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const uint8_t* b,
+                                    const float* sfb, uint16_t* d, const int32_t* masked_m,
+                                    int num_groups, int max_m, int n, int k, int expected_m,
+                                    dg_stream_t stream);
+
+/* Row alignment required of each expert's segment in the contiguous layout (128). */
+int dg_get_m_alignment_for_contiguous_layout(void);
+
+/* Leading dimension of the slab-major sfa layout for m rows: m rounded up to 4. */
+int dg_get_sfa_ld(int m);
+
+/*
+ * Quantise an fp32 activation matrix x[m][k] to e4m3 codes q[m][k] with one
+ * fp32 scale per row and 128-wide slab, written slab-major to
+ * sfa[kb*dg_get_sfa_ld(m) + row] (entries for rows >= m are set to 0).
+ * Per block: amax = max|x| (floored at 1e-4), s = amax / 448 (fp32, correctly
+ * rounded), q = e4m3(x / s) rounded to nearest even and saturated at 448.
+ */
+int dg_quantize_a_1x128(const float* x, uint8_t* q, float* sfa, int m, int k, dg_stream_t stream);
+
+/*
+ * Quantise an fp32 weight matrix x[n][k] to e4m3 codes q[n][k] with one fp32
+ * scale per 128 x 128 block, sfb[ceil(n/128)][k/128]; same rule as above;
+ * the last row block may be partial.
+ */
+int dg_quantize_b_128x128(const float* x, uint8_t* q, float* sfb, int n, int k, dg_stream_t stream);
+
+/* Static text for a status code. */
+const char* dg_status_string(int status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* dg_last_error_message(void);
+
+/* Library version string. */
+const char* dg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_H */

@@ -1,0 +1,103 @@
+"""Helpers shared by the GPU parity tests: move oracle-quantised operands
+into the library's device layouts, run the library, and read results back.
+
+Nothing here computes the method: codes and scales come from the oracle's
+quantisers (CPU), results from the library (GPU), expected values from the
+oracle's GEMMs (CPU).
+"""
+
+import numpy as np
+import torch
+
+import fp8_block_scaled_nt_amd as dg
+
+SENTINEL = 0xFFFF  # bf16 NaN pattern used to prefill D
+
+
+def sfa_ld(m):
+    return (m + 3) // 4 * 4
+
+
+def slab_major(sfa_logical):
+    """Logical [rows, K/128] scales -> the library's slab-major [K/128, ld(rows)]
+    (padding entries zero)."""
+    rows, kb = sfa_logical.shape
+    out = np.zeros((kb, sfa_ld(rows)), dtype=np.float32)
+    out[:, :rows] = sfa_logical.T
+    return out
+
+
+def slab_major_to_logical(sfa_dev, rows):
+    """Inverse of slab_major for a downloaded buffer."""
+    return np.ascontiguousarray(sfa_dev[:, :rows].T)
+
+
+def codes_to_device(codes, dev):
+    return torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).to(dev).view(torch.float8_e4m3fn)
+
+
+def f32_to_device(x, dev):
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev)
+
+
+def sentinel_bf16(shape, dev, guard=0):
+    """A bf16 buffer prefilled with the sentinel, with `guard` extra trailing
+    elements; returns (view of the requested shape, the whole flat buffer)."""
+    numel = int(np.prod(shape))
+    flat = torch.full((numel + guard,), SENTINEL, dtype=torch.uint16, device=dev)
+    view = flat[:numel].view(torch.bfloat16).view(*shape)
+    return view, flat
+
+
+def d_bits(d):
+    return d.view(torch.uint16).cpu().numpy()
+
+
+def d_float(d):
+    return d.float().cpu().numpy().astype(np.float64)
+
+
+def run_dense(qa, sa, qb, sb, dev, guard=256):
+    m, k = qa.shape
+    n = qb.shape[0]
+    a = codes_to_device(qa, dev)
+    b = codes_to_device(qb, dev)
+    sfa = f32_to_device(slab_major(sa), dev)
+    sfb = f32_to_device(sb, dev)
+    d, flat = sentinel_bf16((m, n), dev, guard)
+    dg.fp8_gemm_nt((a, sfa), (b, sfb), d)
+    torch.cuda.synchronize()
+    return d, flat
+
+
+def run_contiguous(qa, sa, qb, sb, m_indices, dev, guard=256):
+    m, k = qa.shape
+    g, n, _ = qb.shape
+    a = codes_to_device(qa, dev)
+    b = codes_to_device(qb, dev)
+    sfa = f32_to_device(slab_major(sa), dev)
+    sfb = f32_to_device(sb, dev)
+    idx = torch.from_numpy(np.asarray(m_indices, np.int32)).to(dev)
+    d, flat = sentinel_bf16((m, n), dev, guard)
+    dg.m_grouped_fp8_gemm_nt_contiguous((a, sfa), (b, sfb), d, idx)
+    torch.cuda.synchronize()
+    return d, flat
+
+
+def run_masked(qa, sa, qb, sb, masked_m, dev, expected_m=0, guard=256):
+    g, max_m, k = qa.shape
+    n = qb.shape[1]
+    a = codes_to_device(qa, dev)
+    b = codes_to_device(qb, dev)
+    sfa = f32_to_device(np.stack([slab_major(sa[i]) for i in range(g)]), dev)
+    sfb = f32_to_device(sb, dev)
+    mm = torch.from_numpy(np.asarray(masked_m, np.int32)).to(dev)
+    d, flat = sentinel_bf16((g, max_m, n), dev, guard)
+    dg.m_grouped_fp8_gemm_nt_masked((a, sfa), (b, sfb), d, mm, expected_m)
+    torch.cuda.synchronize()
+    return d, flat
+
+
+def guard_untouched(flat, numel):
+    tail = flat[numel:].cpu().numpy()
+    return bool(np.all(tail == SENTINEL))

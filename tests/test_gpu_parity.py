@@ -1,0 +1,126 @@
+"""GPU parity: the library's GEMMs against the oracle, element by element.
+
+Operands are drawn by `workloads`, quantised on the CPU by the oracle, and
+the same bytes are given to the GPU, so these tests check the GEMM alone.
+Sizes span several tiles of every configuration and ragged tails in M and N
+(N=2112 has a 64-row partial scale block).  The acceptance rule is
+|d - r| <= 8e-3 |r| + 1e-3 rms(r) over valid elements; every element without
+a result must keep the 0xFFFF sentinel, and the guard band past D must stay
+untouched.
+"""
+
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+DENSE_CONFIGS = ["dense_256x256_w8", "dense_128x128_w4", "dense_64x64_w4"]
+
+
+def dense_case(m, n, k, seed, b_std=1.0):
+    x = W.draw_dense(m, n, k, seed=seed, b_std=b_std)
+    qa, sa = oracle.quantize_a_1x128(x["a"])
+    qb, sb = oracle.quantize_b_128x128(x["b"])
+    return qa, sa, qb, sb
+
+
+def check_dense(gpu, qa, sa, qb, sb, label):
+    print(f"[case] {label}", flush=True)
+    d, flat = H.run_dense(qa, sa, qb, sb, gpu)
+    r = oracle.gemm_nt_ref(qa, sa, qb, sb)
+    res = oracle.tolerance_check(H.d_float(d), r)
+    assert res["ok"], (label, res)
+    assert H.guard_untouched(flat, d.numel()), label
+    return d
+
+
+@pytest.mark.parametrize("m,n,k", [
+    (128, 512, 1024),   # the small dense workload
+    (1, 16, 128),
+    (17, 40, 256),
+    (200, 176, 384),
+    (64, 2112, 512),
+    (300, 520, 640),
+    (513, 257, 256),
+])
+def test_dense_default_selection(gpu, m, n, k):
+    check_dense(gpu, *dense_case(m, n, k, seed=m + n + k), label=f"dense {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("cfg", DENSE_CONFIGS)
+@pytest.mark.parametrize("m,n,k", [(300, 520, 640), (64, 200, 384), (520, 300, 256)])
+def test_dense_every_config(gpu, cfg, m, n, k, monkeypatch):
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    check_dense(gpu, *dense_case(m, n, k, seed=7), label=f"{cfg} {m}x{n}x{k}")
+
+
+def test_dense_small_workload_matches(gpu):
+    x = W.draw("dense_128x512x1024")
+    qa, sa = oracle.quantize_a_1x128(x["a"])
+    qb, sb = oracle.quantize_b_128x128(x["b"])
+    d = check_dense(gpu, qa, sa, qb, sb, "dense_128x512x1024 seed 0")
+    # run-to-run determinism (no atomics in the GEMM)
+    d2, _ = H.run_dense(qa, sa, qb, sb, gpu)
+    assert np.array_equal(H.d_bits(d), H.d_bits(d2))
+
+
+def test_dense_unit_scale_exact_values(gpu):
+    # all-ones operands with unit scales: every output is exactly k
+    m, n, k = 96, 144, 1024
+    qa = np.full((m, k), 0x38, np.uint8)
+    qb = np.full((n, k), 0x38, np.uint8)
+    d, _ = H.run_dense(qa, np.ones((m, 8), np.float32), qb, np.ones((2, 8), np.float32), gpu)
+    assert np.all(H.d_float(d) == k)
+
+
+@pytest.mark.parametrize("cfg", [None, "contig_128x256_w8", "contig_128x128_w4"])
+def test_contiguous(gpu, cfg, monkeypatch):
+    if cfg:
+        monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    group_rows = [200, 0, 77, 128, 5]
+    n, k = 384, 512
+    x = W.draw_contiguous(group_rows, n, k, seed=3)
+    idx = x["m_indices"].copy()
+    idx[5] = 99  # an out-of-range tag inside expert 0's block: no result
+    qa, sa = oracle.quantize_a_1x128(x["a"])
+    qbs = [oracle.quantize_b_128x128(x["b"][g]) for g in range(len(group_rows))]
+    qb = np.stack([q for q, _ in qbs])
+    sb = np.stack([s for _, s in qbs])
+    print(f"[case] contiguous {cfg} rows={group_rows}", flush=True)
+    d, flat = H.run_contiguous(qa, sa, qb, sb, idx, gpu)
+    r, valid = oracle.grouped_contiguous_ref(qa, sa, qb, sb, idx)
+    res = oracle.tolerance_check(H.d_float(d), r, valid[:, None])
+    assert res["ok"], res
+    bits = H.d_bits(d)
+    assert np.all(bits[~valid] == H.SENTINEL)
+    assert H.guard_untouched(flat, d.numel())
+
+
+@pytest.mark.parametrize("cfg,max_m", [(None, 96), (None, 256), ("masked_256x128_w4", 300),
+                                       ("masked_64x64_w4", 130)])
+def test_masked(gpu, cfg, max_m, monkeypatch):
+    if cfg:
+        monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    g, n, k = 6, 272, 384
+    masked_m = np.array([0, 1, 17, max_m, max_m + 50, max_m // 2 + 3], dtype=np.int32)
+    x = W.draw_masked(g, max_m, n, k, seed=4, masked_m=masked_m)
+    qas = [oracle.quantize_a_1x128(x["a"][i]) for i in range(g)]
+    qa = np.stack([q for q, _ in qas])
+    sa = np.stack([s for _, s in qas])
+    qbs = [oracle.quantize_b_128x128(x["b"][i]) for i in range(g)]
+    qb = np.stack([q for q, _ in qbs])
+    sb = np.stack([s for _, s in qbs])
+    print(f"[case] masked {cfg} max_m={max_m}", flush=True)
+    d, flat = H.run_masked(qa, sa, qb, sb, masked_m, gpu)
+    r, valid = oracle.grouped_masked_ref(qa, sa, qb, sb, masked_m)
+    res = oracle.tolerance_check(H.d_float(d), r, valid[:, :, None])
+    assert res["ok"], res
+    bits = H.d_bits(d)
+    assert np.all(bits[~valid] == H.SENTINEL)
+    assert H.guard_untouched(flat, d.numel())
