@@ -1,0 +1,319 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8 block-scaled NT GEMM hot path on one MI355X.
+
+A step is one pass of the hot path over one batch: quantise the fp32
+activations to e4m3 with 1x128 scales, then the FP8 NT GEMM with the
+128x128-scaled weights (quantised once beforehand, as weights are).  The
+headline workload is the dense decode shape M=64 N=2112 K=7168 (activations
+N(0,1), weights N(0,0.02), seed 0), reported as HBM GB/s of algorithmic bytes.
+
+Measurements
+  * value / ms_per_step: K steps captured in one HIP graph, replayed once,
+    bracketed by torch.cuda.synchronize() and the host clock.  Each step uses
+    a different copy of the operands (rotation over > 512 MiB) so no step is
+    served from the 256 MiB Infinity Cache.
+  * roofline: the GEMM kernel alone, its own duration from events recorded at
+    kernel start and end (hipExtLaunchKernel through dg_profile_next_launch),
+    averaged over the timed launches.
+  * cpu_baseline: the CPU oracle (numpy, fp64) running the same step on the
+    host for a bounded sample.
+  * extra: every other workload's GEMM kernel timed the same way.
+
+Prints one JSON line on stdout.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
+ROTATE_BYTES = 600 << 20       # > 2x the 256 MiB Infinity Cache
+MAIN_WORKLOAD = "dense_decode_64x2112x7168"
+METRIC = "FP8 block-scaled GEMM TFLOPS (large) & HBM GB/s (decode) on 1 GPU; % of roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--kernel-launches", type=int, default=200,
+                    help="timed GEMM launches per workload for the kernel figures")
+    ap.add_argument("--workloads", default="all",
+                    help="'all', 'main', or a comma list of workload names for the extra figures")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    return ap.parse_args()
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp8_block_scaled_nt_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel_key)
+    if not e or e.get("source_hash") != source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+class Rotation:
+    """R copies of one workload's device operands, R chosen so the copies span
+    more than the Infinity Cache."""
+
+    def __init__(self, make_set, set_bytes):
+        self.r = max(2, -(-ROTATE_BYTES // max(set_bytes, 1)))
+        self.sets = [make_set(i) for i in range(self.r)]
+
+    def __getitem__(self, i):
+        return self.sets[i % self.r]
+
+
+def kernel_time_us(torch, dg, launch, rot, n_launch, warm=5):
+    """Average duration of the GEMM kernel itself over n_launch launches."""
+    for i in range(warm):
+        launch(rot[i])
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_launch)]
+    stops = [torch.cuda.Event(enable_timing=True) for _ in range(n_launch)]
+    for e in starts + stops:
+        e.record()  # materialise the underlying HIP events
+    torch.cuda.synchronize()
+    for i in range(n_launch):
+        dg.profile_next_launch(starts[i], stops[i])
+        launch(rot[i])
+    torch.cuda.synchronize()
+    times = sorted(starts[i].elapsed_time(stops[i]) * 1e3 for i in range(n_launch))
+    return sum(times) / len(times), times[len(times) // 2]
+
+
+def setup_workload(torch, np, dg, W, name, dev):
+    """Device operands for one workload, quantised by the library's own
+    quantisers; returns (kind, params, rotation, launch, inputs)."""
+    w = W.WORKLOADS[name]
+    s = w.shape
+    inp = W.draw(name)
+    if w.kind == "dense":
+        m, n, k = s["m"], s["n"], s["k"]
+        xa = torch.from_numpy(inp["a"]).to(dev)
+        xb = torch.from_numpy(inp["b"]).to(dev)
+        qb, sfb = dg.quantize_b_128x128(xb)
+        del xb
+
+        def make(i):
+            qa, sfa = dg.quantize_a_1x128(xa)
+            d = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            return {"xa": xa.clone() if i else xa, "qa": qa, "sfa": sfa,
+                    "qb": qb.clone() if i else qb, "sfb": sfb.clone(), "d": d}
+
+        set_bytes = m * k * 5 + n * k + 2 * m * n
+        rot = Rotation(make, set_bytes)
+
+        def launch(st):
+            dg.fp8_gemm_nt((st["qa"], st["sfa"]), (st["qb"], st["sfb"]), st["d"])
+
+        def quant(st):
+            dg.quantize_a_1x128(st["xa"], st["qa"], st["sfa"])
+
+        return w.kind, dict(m=m, n=n, k=k), rot, launch, quant, inp
+    if w.kind == "contiguous":
+        n, k = s["n"], s["k"]
+        idx = torch.from_numpy(inp["m_indices"]).to(dev)
+        m = idx.numel()
+        xa = torch.from_numpy(inp["a"]).to(dev)
+        qb, sfb = dg.quantize_b_128x128(torch.from_numpy(inp["b"]).to(dev))
+        qa, sfa = dg.quantize_a_1x128(xa)
+        del xa
+
+        def make(i):
+            d = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            if i == 0:
+                return {"qa": qa, "sfa": sfa, "qb": qb, "sfb": sfb, "d": d, "idx": idx}
+            return {"qa": qa.clone(), "sfa": sfa.clone(), "qb": qb.clone(), "sfb": sfb.clone(),
+                    "d": d, "idx": idx.clone()}
+
+        rot = Rotation(make, m * k + qb.numel() + 2 * m * n)
+
+        def launch(st):
+            dg.m_grouped_fp8_gemm_nt_contiguous((st["qa"], st["sfa"]), (st["qb"], st["sfb"]), st["d"], st["idx"])
+
+        return w.kind, dict(m_indices=inp["m_indices"], g=len(s["group_rows"]), n=n, k=k), rot, launch, None, inp
+    g, max_m, n, k = s["g"], s["max_m"], s["n"], s["k"]
+    mm = torch.from_numpy(inp["masked_m"]).to(dev)
+    qa, sfa = dg.quantize_a_1x128(torch.from_numpy(inp["a"]).to(dev))
+    qb, sfb = dg.quantize_b_128x128(torch.from_numpy(inp["b"]).to(dev))
+
+    def make(i):
+        d = torch.empty((g, max_m, n), dtype=torch.bfloat16, device=dev)
+        if i == 0:
+            return {"qa": qa, "sfa": sfa, "qb": qb, "sfb": sfb, "d": d, "mm": mm}
+        return {"qa": qa.clone(), "sfa": sfa.clone(), "qb": qb.clone(), "sfb": sfb.clone(), "d": d,
+                "mm": mm.clone()}
+
+    rot = Rotation(make, qa.numel() + qb.numel() + 2 * g * max_m * n)
+    expected = int(np.clip(inp["masked_m"], 0, max_m).mean())
+
+    def launch(st):
+        dg.m_grouped_fp8_gemm_nt_masked((st["qa"], st["sfa"]), (st["qb"], st["sfb"]), st["d"], st["mm"], expected)
+
+    return w.kind, dict(masked_m=inp["masked_m"], max_m=max_m, n=n, k=k), rot, launch, None, inp
+
+
+def cpu_oracle_baseline(np, W, inp, m, n, k, seconds):
+    """Time the oracle doing the main step (quantise A, GEMM) on the host."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - informational only
+        threads = 1
+    qb, sb = oracle.quantize_b_128x128(inp["b"])  # weights: outside the timed loop
+    flops, gemm_bytes = W.algorithmic_work("dense", m=m, n=n, k=k)
+    step_bytes = gemm_bytes + m * k * 4 + m * k + 4 * m * (k // 128)
+    t0 = time.perf_counter()
+    iters = 0
+    while True:
+        qa, sa = oracle.quantize_a_1x128(inp["a"])
+        oracle.gemm_nt_ref(qa, sa, qb, sb)
+        iters += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": step_bytes * iters / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole decode step (quantise A 64x7168, fp64 GEMM 64x2112x7168) "
+                      f"x{iters} in {el:.1f} s; {flops * iters / el / 1e9:.2f} GFLOP/s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    import fp8_block_scaled_nt_amd as dg
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+
+    # ---- headline step: quantise A + GEMM on the decode shape
+    kind, params, rot, launch, quant, inp = setup_workload(torch, np, dg, W, MAIN_WORKLOAD, dev)
+    m, n, k = params["m"], params["n"], params["k"]
+    flops, gemm_bytes = W.algorithmic_work("dense", m=m, n=n, k=k)
+    quant_bytes = m * k * 4 + m * k + 4 * m * (k // 128)
+    step_bytes = gemm_bytes + quant_bytes
+
+    def step(i):
+        st = rot[i]
+        quant(st)
+        launch(st)
+
+    for i in range(min(args.warmup, 8)):  # eager warm-up before capture
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    g_warm = torch.cuda.CUDAGraph()
+    g_main = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g_warm, stream=stream):
+            for i in range(args.warmup):
+                step(i)
+        with torch.cuda.graph(g_main, stream=stream):
+            for i in range(args.steps):
+                step(i)
+    torch.cuda.synchronize()
+    g_warm.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g_main.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    value = step_bytes * args.steps / wall / 1e9
+
+    # ---- the GEMM kernel alone, timed at the kernel
+    avg_us, med_us = kernel_time_us(torch, dg, launch, rot, args.kernel_launches)
+    achieved = gemm_bytes / (avg_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(MAIN_WORKLOAD),
+                "kernel": "gemm_fp8_nt_kernel (dense)", "kernel_avg_us": round(avg_us, 3),
+                "kernel_median_us": round(med_us, 3), "algorithmic_bytes": gemm_bytes}
+
+    # ---- other workloads: GEMM kernel figures
+    extra = {}
+    names = [] if args.workloads == "main" else (
+        [x for x in W.WORKLOADS if x != MAIN_WORKLOAD] if args.workloads == "all" else args.workloads.split(","))
+    del rot
+    torch.cuda.empty_cache()
+    for name in names:
+        kind_x, p_x, rot_x, launch_x, _, inp_x = setup_workload(torch, np, dg, W, name, dev)
+        fl, by = W.algorithmic_work(kind_x, **p_x)
+        a_us, md_us = kernel_time_us(torch, dg, launch_x, rot_x, max(10, args.kernel_launches // 4))
+        tf = fl / (a_us * 1e-6) / 1e12
+        gbs = by / (a_us * 1e-6) / 1e9
+        bound = "mfma" if fl / by > FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
+        extra[name] = {"kernel_avg_us": round(a_us, 2), "kernel_median_us": round(md_us, 2),
+                       "tflops": round(tf, 1), "gbs": round(gbs, 1), "bound": bound,
+                       "frac": round(tf / FP8_PEAK_TFLOPS if bound == "mfma" else gbs / HBM_PEAK_GBS, 4),
+                       "algorithmic_flops": fl, "algorithmic_bytes": by}
+        print(f"[bench] {name}: {a_us:.1f} us, {tf:.1f} TFLOP/s, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+        del rot_x, inp_x
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_oracle_baseline(np, W, inp, m, n, k, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3 (fp32 promotion, bf16 out)",
+        "data": "synthetic (numpy default_rng(0): activations N(0,1), weights N(0,0.02))",
+        "config": {"workload": MAIN_WORKLOAD, "m": m, "n": n, "k": k,
+                   "step": "quantise A 1x128 + FP8 NT GEMM (B quantised 128x128 once)",
+                   "step_algorithmic_bytes": step_bytes, "gemm_algorithmic_flops": flops,
+                   "rotation_sets": "operand copies > 512 MiB, one per step", "graph": True,
+                   "gpu": props.name, "cus": props.multi_processor_count},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_PKG_DIR, "libdg.so")
 __all__ = [
     "DGError", "lib", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous",
     "m_grouped_fp8_gemm_nt_masked", "quantize_a_1x128", "quantize_b_128x128",
-    "get_m_alignment_for_contiguous_layout", "get_sfa_ld", "empty_sfa",
+    "get_m_alignment_for_contiguous_layout", "get_sfa_ld", "empty_sfa", "profile_next_launch",
 ]
 
 
@@ -50,6 +50,7 @@ _SIGNATURES = {
     "dg_status_string": [_ci],
     "dg_last_error_message": [],
     "dg_version": [],
+    "dg_profile_next_launch": [_vp, _vp],
 }
 _RESTYPES = {"dg_status_string": ctypes.c_char_p, "dg_last_error_message": ctypes.c_char_p,
              "dg_version": ctypes.c_char_p}
@@ -98,6 +99,13 @@ def _need(t, name, dtypes, ndim):
         raise ValueError(f"{name} must be a device tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def profile_next_launch(start_event, stop_event):
+    """Make the next GEMM launch on this thread record the two torch.cuda.Event
+    objects (timing enabled, already recorded once so they exist) at the start
+    and end of the kernel itself."""
+    _check(lib().dg_profile_next_launch(start_event._as_parameter_, stop_event._as_parameter_))
 
 
 def get_m_alignment_for_contiguous_layout():

@@ -8,6 +8,7 @@
 // synchronisation.
 #include "../../include/dg.h"
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -24,6 +25,9 @@
 namespace {
 
 thread_local std::string g_last_error;
+// one-shot profiling events for the next GEMM launch on this thread
+thread_local hipEvent_t g_prof_start = nullptr;
+thread_local hipEvent_t g_prof_stop = nullptr;
 
 int fail(int status, const char* fmt, ...) {
   char buf[512];
@@ -150,7 +154,14 @@ int launch(const Config& c, dg::GemmParams& p, int grid, hipStream_t stream) {
             p.k, p.num_groups, grid, c.threads(), c.smem);
   if (grid <= 0) return ok();
   void* args[] = {&p};
-  hipError_t e = hipLaunchKernel(c.fn, dim3(grid), dim3(c.threads()), args, c.smem, stream);
+  hipError_t e;
+  if (g_prof_start || g_prof_stop) {
+    e = hipExtLaunchKernel(c.fn, dim3(grid), dim3(c.threads()), args, c.smem, stream, g_prof_start,
+                           g_prof_stop, 0);
+    g_prof_start = g_prof_stop = nullptr;
+  } else {
+    e = hipLaunchKernel(c.fn, dim3(grid), dim3(c.threads()), args, c.smem, stream);
+  }
   if (e != hipSuccess) return fail(DG_ERR_HIP, "launch of %s failed: %s", c.name, hipGetErrorString(e));
   return ok();
 }
@@ -183,6 +194,12 @@ int dg_get_m_alignment_for_contiguous_layout(void) { return 128; }
 int dg_get_sfa_ld(int m) { return m < 0 ? 0 : sfa_ld(m); }
 
 const char* dg_version(void) { return "dg-gfx950 0.1"; }
+
+int dg_profile_next_launch(void* start_event, void* stop_event) {
+  g_prof_start = (hipEvent_t)start_event;
+  g_prof_stop = (hipEvent_t)stop_event;
+  return ok();
+}
 
 const char* dg_status_string(int status) {
   switch (status) {

@@ -131,6 +131,16 @@ const char* dg_status_string(int status);
 /* Detail of the last failure on the calling thread ("" if none). */
 const char* dg_last_error_message(void);
 
+/*
+ * Profiling hook: the next GEMM launch made on the calling thread records
+ * `start_event` and `stop_event` (hipEvent_t handles created by the caller
+ * with timing enabled; either may be NULL) at the start and end of the
+ * kernel itself (hipExtLaunchKernel), so hipEventElapsedTime gives the
+ * kernel's own duration without launch gaps.  One-shot: the hook clears
+ * itself after that launch.  Not graph-capturable; for measurement only.
+ */
+int dg_profile_next_launch(void* start_event, void* stop_event);
+
 /* Library version string. */
 const char* dg_version(void);
 

@@ -1,0 +1,96 @@
+"""The C ABI library loads on the CPU, exports every function include/dg.h
+declares, and rejects bad arguments on the host before touching a device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_block_scaled_nt_amd as dg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dg.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return dg.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(lib, name), name
+        assert name in dg._SIGNATURES, f"binding lacks {name}"
+
+
+def test_host_only_functions(lib):
+    assert lib.dg_get_m_alignment_for_contiguous_layout() == 128
+    assert [lib.dg_get_sfa_ld(m) for m in (0, 1, 4, 5, 64, 2067)] == [0, 4, 4, 8, 64, 2068]
+    assert lib.dg_status_string(0) == b"ok"
+    assert lib.dg_status_string(3) == b"misaligned pointer"
+    assert lib.dg_version().startswith(b"dg-gfx950")
+
+
+P = ctypes.c_void_p
+GOOD = P(0x10000)  # never dereferenced: every case below fails validation first
+ODD = P(0x10004)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, GOOD, GOOD, GOOD, GOOD, 64, 64, 128), 1),      # null a
+    ((GOOD, GOOD, GOOD, GOOD, GOOD, -1, 64, 128), 1),      # negative m
+    ((GOOD, GOOD, GOOD, GOOD, GOOD, 64, 0, 128), 1),       # n = 0
+    ((GOOD, GOOD, GOOD, GOOD, GOOD, 64, 64, 100), 2),      # k not a multiple of 128
+    ((GOOD, GOOD, GOOD, GOOD, GOOD, 64, 64, 0), 2),
+    ((GOOD, ODD, GOOD, GOOD, GOOD, 64, 64, 128), 3),       # misaligned sfa
+    ((GOOD, GOOD, GOOD, GOOD, GOOD, 0, 64, 128), 0),       # m = 0: no-op, no device needed
+])
+def test_dense_validation(lib, args, status):
+    assert lib.dg_fp8_gemm_nt(*args, None) == status
+    if status:
+        assert len(lib.dg_last_error_message()) > 0
+
+
+def test_grouped_validation(lib):
+    f = lib.dg_m_grouped_fp8_gemm_nt_contiguous
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, None, 128, 64, 128, 2, None) == 1
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 100, 64, 128, 2, None) == 2  # m not 128-aligned
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 128, 64, 128, 0, None) == 1  # no groups
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 0, 64, 128, 2, None) == 0
+    g = lib.dg_m_grouped_fp8_gemm_nt_masked
+    assert g(GOOD, GOOD, GOOD, GOOD, GOOD, None, 4, 64, 64, 128, 0, None) == 1
+    assert g(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 4, -1, 64, 128, 0, None) == 1
+    assert g(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 4, 64, 64, 256 + 1, 0, None) == 2
+    assert g(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 0, 64, 64, 128, 0, None) == 0
+    assert g(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 4, 0, 64, 128, 0, None) == 0
+
+
+def test_quant_validation(lib):
+    assert lib.dg_quantize_a_1x128(None, GOOD, GOOD, 4, 128, None) == 1
+    assert lib.dg_quantize_a_1x128(GOOD, GOOD, GOOD, 4, 130, None) == 2
+    assert lib.dg_quantize_b_128x128(GOOD, ODD, GOOD, 4, 128, None) == 3
+    assert lib.dg_quantize_b_128x128(GOOD, GOOD, GOOD, 0, 128, None) == 0
+
+
+def test_no_device_is_reported_not_crashed(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    # valid-looking arguments reach the device query, which reports no device
+    assert lib.dg_fp8_gemm_nt(GOOD, GOOD, GOOD, GOOD, GOOD, 64, 64, 128, None) == 4
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(dg, "_lib", None)
+    monkeypatch.setattr(dg, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        dg.lib()
