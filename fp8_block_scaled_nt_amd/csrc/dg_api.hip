@@ -86,34 +86,38 @@ int current_device(int* dev, DeviceInfo** info) {
   return DG_OK;
 }
 
-// ---- tile configurations
+// ---- tile configurations (compile-time instantiations; the host picks one)
 struct Config {
   const char* name;
-  int variant, bm, bn, wm, wn;
+  int variant, bm, bn, wm, wn, nst;
   const void* fn;
   int smem;
   int threads() const { return wm * wn * 64; }
 };
 
-template <int BM, int BN, int WM, int WN, int VAR>
+template <int BM, int BN, int WM, int WN, int NST, int VAR>
 Config make_config(const char* name) {
-  return Config{name, VAR, BM, BN, WM, WN,
-                reinterpret_cast<const void*>(&dg::gemm_fp8_nt_kernel<BM, BN, WM, WN, VAR>),
-                dg::Smem<BM, BN>::kBytes};
+  return Config{name, VAR, BM, BN, WM, WN, NST,
+                reinterpret_cast<const void*>(&dg::gemm_fp8_nt_kernel<BM, BN, WM, WN, NST, VAR>),
+                dg::Smem<BM, BN, NST>::kBytes};
 }
 
 const Config* configs(int* count) {
   static const Config table[] = {
       // dense
-      make_config<256, 256, 2, 4, dg::kDense>("dense_256x256_w8"),
-      make_config<128, 128, 2, 2, dg::kDense>("dense_128x128_w4"),
-      make_config<64, 64, 1, 4, dg::kDense>("dense_64x64_w4"),
+      make_config<256, 256, 2, 4, 2, dg::kDense>("dense_256x256_w8_s2"),
+      make_config<256, 128, 4, 2, 3, dg::kDense>("dense_256x128_w8_s3"),
+      make_config<128, 256, 2, 4, 3, dg::kDense>("dense_128x256_w8_s3"),
+      make_config<128, 128, 2, 2, 3, dg::kDense>("dense_128x128_w4_s3"),
+      make_config<128, 128, 2, 2, 2, dg::kDense>("dense_128x128_w4_s2"),
+      make_config<64, 64, 1, 4, 3, dg::kDense>("dense_64x64_w4_s3"),
       // contiguous (block rows <= the 128-row alignment)
-      make_config<128, 256, 2, 4, dg::kContiguous>("contig_128x256_w8"),
-      make_config<128, 128, 2, 2, dg::kContiguous>("contig_128x128_w4"),
+      make_config<128, 256, 2, 4, 3, dg::kContiguous>("contig_128x256_w8_s3"),
+      make_config<128, 128, 2, 2, 3, dg::kContiguous>("contig_128x128_w4_s3"),
       // masked
-      make_config<256, 128, 1, 4, dg::kMasked>("masked_256x128_w4"),
-      make_config<64, 64, 1, 4, dg::kMasked>("masked_64x64_w4"),
+      make_config<256, 128, 1, 4, 2, dg::kMasked>("masked_256x128_w4_s2"),
+      make_config<256, 128, 1, 4, 3, dg::kMasked>("masked_256x128_w4_s3"),
+      make_config<64, 64, 1, 4, 3, dg::kMasked>("masked_64x64_w4_s3"),
   };
   *count = sizeof(table) / sizeof(table[0]);
   return table;
@@ -127,10 +131,19 @@ const Config* find_config(const char* name, int variant) {
   return nullptr;
 }
 
-const Config* forced_config(int variant) {
+// DG_FORCE_CONFIG=<name> pins the configuration of the variant it names (for
+// tuning sweeps); an unknown name is an error rather than silently ignored.
+int forced_config(int variant, const Config** out) {
+  *out = nullptr;
   const char* e = getenv("DG_FORCE_CONFIG");
-  if (!e || !*e) return nullptr;
-  return find_config(e, variant);
+  if (!e || !*e) return DG_OK;
+  int cnt = 0;
+  const Config* t = configs(&cnt);
+  bool known = false;
+  for (int i = 0; i < cnt; ++i) known = known || strcmp(t[i].name, e) == 0;
+  if (!known) return fail(DG_ERR_INVALID_ARGUMENT, "DG_FORCE_CONFIG names no configuration: %s", e);
+  *out = find_config(e, variant);
+  return DG_OK;
 }
 
 std::once_flag g_attr_once;
@@ -182,6 +195,16 @@ int check_k_n(int n, int k) {
   if (n < 1) return fail(DG_ERR_INVALID_ARGUMENT, "n must be >= 1 (got %d)", n);
   if (k < 128 || k % 128 != 0)
     return fail(DG_ERR_UNSUPPORTED_SHAPE, "k must be a positive multiple of 128 (got %d)", k);
+  if ((long long)n * k > 0xFFFFFFFFLL)
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "one B operand must stay below 4 GiB (n*k = %lld)", (long long)n * k);
+  return DG_OK;
+}
+
+// The kernels address one operand matrix (one expert's, for the grouped
+// layouts) with 32-bit byte offsets.
+int check_rows(long long rows, int k) {
+  if (rows * k > 0xFFFFFFFFLL)
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "one A operand must stay below 4 GiB (rows*k = %lld)", rows * k);
   return DG_OK;
 }
 
@@ -221,17 +244,19 @@ int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const f
   if (!a || !sfa || !b || !sfb || !d) return fail(DG_ERR_INVALID_ARGUMENT, "null pointer argument");
   if (m < 0) return fail(DG_ERR_INVALID_ARGUMENT, "m must be >= 0 (got %d)", m);
   if (int s = check_k_n(n, k)) return s;
+  if (int s = check_rows(m, k)) return s;
   if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d))
     return fail(DG_ERR_MISALIGNED, "pointers must be 16-byte aligned");
   if (m == 0) return ok();
   int dev;
   DeviceInfo* info;
   if (int s = current_device(&dev, &info)) return s;
-  const Config* c = forced_config(dg::kDense);
+  const Config* c;
+  if (int s = forced_config(dg::kDense, &c)) return s;
   if (!c) {
-    if (m <= 64) c = find_config("dense_64x64_w4", dg::kDense);
-    else if (m <= 256 || n <= 256) c = find_config("dense_128x128_w4", dg::kDense);
-    else c = find_config("dense_256x256_w8", dg::kDense);
+    if (m <= 64) c = find_config("dense_64x64_w4_s3", dg::kDense);
+    else if (m <= 256 || n <= 256) c = find_config("dense_128x128_w4_s3", dg::kDense);
+    else c = find_config("dense_256x256_w8_s2", dg::kDense);
   }
   dg::GemmParams p{};
   p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d;
@@ -251,6 +276,7 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, cons
   if (int s = check_k_n(n, k)) return s;
   if (m % 128 != 0)
     return fail(DG_ERR_UNSUPPORTED_SHAPE, "m must be a multiple of the 128-row alignment (got %d)", m);
+  if (int s = check_rows(m, k)) return s;
   if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d) ||
       (reinterpret_cast<uintptr_t>(m_indices) & 3u))
     return fail(DG_ERR_MISALIGNED, "pointers must be 16-byte aligned (m_indices 4-byte)");
@@ -258,8 +284,9 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, cons
   int dev;
   DeviceInfo* info;
   if (int s = current_device(&dev, &info)) return s;
-  const Config* c = forced_config(dg::kContiguous);
-  if (!c) c = find_config(n >= 256 ? "contig_128x256_w8" : "contig_128x128_w4", dg::kContiguous);
+  const Config* c;
+  if (int s = forced_config(dg::kContiguous, &c)) return s;
+  if (!c) c = find_config(n >= 256 ? "contig_128x256_w8_s3" : "contig_128x128_w4_s3", dg::kContiguous);
   dg::GemmParams p{};
   p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.m_indices = m_indices;
   p.num_groups = num_groups;
@@ -278,6 +305,7 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const ui
   if (max_m < 0) return fail(DG_ERR_INVALID_ARGUMENT, "max_m must be >= 0 (got %d)", max_m);
   if (expected_m < 0) return fail(DG_ERR_INVALID_ARGUMENT, "expected_m must be >= 0 (got %d)", expected_m);
   if (int s = check_k_n(n, k)) return s;
+  if (int s = check_rows(max_m, k)) return s;
   if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d) ||
       (reinterpret_cast<uintptr_t>(masked_m) & 3u))
     return fail(DG_ERR_MISALIGNED, "pointers must be 16-byte aligned (masked_m 4-byte)");
@@ -285,8 +313,9 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const ui
   int dev;
   DeviceInfo* info;
   if (int s = current_device(&dev, &info)) return s;
-  const Config* c = forced_config(dg::kMasked);
-  if (!c) c = find_config(max_m <= 64 ? "masked_64x64_w4" : "masked_256x128_w4", dg::kMasked);
+  const Config* c;
+  if (int s = forced_config(dg::kMasked, &c)) return s;
+  if (!c) c = find_config(max_m <= 64 ? "masked_64x64_w4_s3" : "masked_256x128_w4_s2", dg::kMasked);
   dg::GemmParams p{};
   p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.masked_m = masked_m;
   p.num_groups = num_groups;

@@ -14,11 +14,13 @@
 //    slab (the MFMA's own E8M0 scales stay neutral: the fp32 block scales
 //    are not powers of two);
 //  * operand tiles move HBM/L2 -> LDS with global_load_lds_dwordx4 (no VGPR
-//    staging), double buffered, one workgroup barrier per slab;
-//  * the LDS tile is stored fragment-major: every 1 KiB holds exactly what
-//    one ds_read_b128 of a whole wave needs, so LDS reads are contiguous per
-//    wave (free of bank conflicts for any bank count) and each DMA
-//    instruction writes one such 1 KiB block;
+//    staging), NST-stage buffered, one workgroup barrier per slab;
+//  * each DMA instruction reads 8 whole 128-byte rows (8 lanes per cache
+//    line): on gfx950 this moves ~3.7x more bytes per clock into a CU than
+//    instructions that cover 16 half lines.  LDS keeps the tile row-major,
+//    128 bytes per row, with the 16-byte chunk c of tile row r stored in
+//    slot c ^ ((r >> 1) & 7): the 16 rows a fragment read touches then hit
+//    16 distinct 16-byte bank groups, so ds_read_b128 is conflict-free;
 //  * the blockIdx -> tile map is XCD-aware: the 8 XCDs each take a
 //    contiguous run of a grouped-raster tile order, so tiles that share A
 //    rows or B columns sit in the same L2.
@@ -46,7 +48,7 @@ enum Variant { kDense = 0, kContiguous = 1, kMasked = 2 };
 
 constexpr int kSlab = 128;        // K bytes per slab (one scale per slab)
 constexpr int kNumXcd = 8;        // MI355X: 8 XCDs, workgroups dealt round-robin
-constexpr int kFragBytes = 1024;  // one wave-wide 16-byte-per-lane LDS block
+constexpr int kDmaBytes = 1024;   // LDS bytes one wave-wide 16-byte-per-lane DMA writes
 
 struct GemmParams {
   const uint8_t* a;
@@ -81,10 +83,47 @@ __device__ __forceinline__ void lds_dma4(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)lds_dst, 4, 0, 0);
 }
 
-// Wait for all of this wave's outstanding vector-memory loads (including the
-// LDS DMA ones) to land.  gfx9 s_waitcnt encoding: vmcnt = 0, expcnt and
-// lgkmcnt left at their maxima.
-__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Wait until at most N of this wave's vector-memory loads (LDS DMA included)
+// are outstanding; they retire in issue order.  gfx9 s_waitcnt encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at their maxima.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_vmem_all() { wait_vmem<0>(); }
+
+// vmcnt wait with a wave-uniform run-time count (a scalar branch picks the
+// immediate).  Counts above 47 wait for everything.
+__device__ __forceinline__ void wait_vmem_dyn(int n) {
+#define DG_VM_CASE(i) \
+  case i:             \
+    wait_vmem<i>();   \
+    return;
+  switch (n) {
+    DG_VM_CASE(1) DG_VM_CASE(2) DG_VM_CASE(3) DG_VM_CASE(4) DG_VM_CASE(5) DG_VM_CASE(6) DG_VM_CASE(7)
+    DG_VM_CASE(8) DG_VM_CASE(9) DG_VM_CASE(10) DG_VM_CASE(11) DG_VM_CASE(12) DG_VM_CASE(13) DG_VM_CASE(14)
+    DG_VM_CASE(15) DG_VM_CASE(16) DG_VM_CASE(17) DG_VM_CASE(18) DG_VM_CASE(19) DG_VM_CASE(20) DG_VM_CASE(21)
+    DG_VM_CASE(22) DG_VM_CASE(23) DG_VM_CASE(24) DG_VM_CASE(25) DG_VM_CASE(26) DG_VM_CASE(27) DG_VM_CASE(28)
+    DG_VM_CASE(29) DG_VM_CASE(30) DG_VM_CASE(31) DG_VM_CASE(32) DG_VM_CASE(33) DG_VM_CASE(34) DG_VM_CASE(35)
+    DG_VM_CASE(36) DG_VM_CASE(37) DG_VM_CASE(38) DG_VM_CASE(39) DG_VM_CASE(40) DG_VM_CASE(41) DG_VM_CASE(42)
+    DG_VM_CASE(43) DG_VM_CASE(44) DG_VM_CASE(45) DG_VM_CASE(46) DG_VM_CASE(47)
+    default:
+      wait_vmem<0>();
+      return;
+  }
+#undef DG_VM_CASE
+}
+
+// Workgroup barrier without a memory fence: the caller has already waited for
+// the loads that must be visible.  (__syncthreads() would also wait for every
+// outstanding LDS DMA, prefetches included.)  The empty asm statements keep
+// the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b) {
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
@@ -92,13 +131,21 @@ __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 127, 0, 127);
 }
 
-template <int BM, int BN>
+// LDS layout: NST stages, each holding one slab of the A tile, of the B
+// tile, the A row scales and the B block scales of that slab; the epilogue
+// reuses the space for the bf16 output tile.
+template <int BM, int BN, int NST>
 struct Smem {
   static constexpr int kA = BM * kSlab;
   static constexpr int kB = BN * kSlab;
   static constexpr int kSa = BM * 4;
-  static constexpr int kStage = kA + kB + kSa;
-  static constexpr int kBytes = 2 * kStage;
+  static constexpr int kSbCount = BN / 128 + 2;  // 128-row blocks a BN-wide tile can touch
+  static constexpr int kSb = 256;                // one dword DMA instruction's footprint
+  static constexpr int kStage = kA + kB + kSa + kSb;
+  static constexpr int kOutPitch = BN * 2 + 16;  // bf16 output row pitch (bytes)
+  static constexpr int kOut = BM * kOutPitch;
+  static constexpr int kMain = NST * kStage;
+  static constexpr int kBytes = kMain > kOut ? kMain : kOut;
 };
 
 // Map a linear tile id to (tile_m, tile_n) in grouped raster order: runs of
@@ -119,7 +166,19 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return (bid % kNumXcd) * (nblocks / kNumXcd) + bid / kNumXcd;
 }
 
-template <int BM, int BN, int WM, int WN, int VAR>
+// Number of slab DMA batches a wave has issued after the one of slab kb, at
+// the top of iteration kb: the prologue issues slabs 0..NST-2 and iteration
+// i issues slab i+NST-1 (nothing for slabs >= KB).
+template <int NST>
+__device__ __forceinline__ int loads_ahead(int kb, int KB) {
+  int n = KB - 1 - kb;
+  return n < NST - 2 ? n : NST - 2;
+}
+
+// LDS slot swizzle of tile row r (see the layout note at the top)
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+template <int BM, int BN, int WM, int WN, int NST, int VAR>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p) {
   constexpr int kThreads = WM * WN * 64;
   constexpr int kWaves = WM * WN;
@@ -127,9 +186,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   constexpr int FM = TM / 16, FN = TN / 16;
   constexpr int kJa = BM / 8;  // DMA instructions per slab for A (1 KiB each)
   constexpr int kJb = BN / 8;
-  using S = Smem<BM, BN>;
+  using S = Smem<BM, BN, NST>;
   static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be whole fragments");
   static_assert(BM <= kThreads, "row-tag pass needs one thread per tile row");
+  static_assert(NST >= 2, "pipeline shape");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_expert;
@@ -162,9 +222,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   const uint8_t* B = p.b;
   const float* SFB = p.sfb;
   uint16_t* D = p.d;
-  int row_limit = p.m;   // rows that exist in memory (load clamp)
-  int valid_rows = p.m;  // rows with a result (masked: the expert's count)
-  int expert = 0;
+  const int row_limit = p.m;  // rows that exist in memory (load clamp)
+  int valid_rows = p.m;       // rows with a result (masked: the expert's count)
   if (VAR == kContiguous) {
     if (threadIdx.x == 0) s_expert = -1;
     __syncthreads();
@@ -174,7 +233,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
       if (tag >= 0 && tag < p.num_groups) atomicMax(&s_expert, tag);
     }
     __syncthreads();
-    expert = s_expert;
+    const int expert = s_expert;
     if (expert < 0) return;  // a block of padding rows only
     if (threadIdx.x < BM) s_row_ok[threadIdx.x] = (tag == expert);
     B += (size_t)expert * p.n * p.k;
@@ -192,39 +251,79 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   }
   const int KB = p.kb_count;
   const int K = p.k;
+  // rows worth loading: the masked layout never reads rows past the count
+  const int a_rows = VAR == kMasked ? valid_rows : row_limit;
 
-  // ---- slab loader: one wave-wide DMA instruction moves 1 KiB into LDS
+  // ---- slab loader.  One wave-wide DMA instruction moves 1 KiB (one
+  // fragment half) into LDS; each wave owns a fixed set of instructions whose
+  // per-lane source offsets are computed once per tile.
+  constexpr int kPerWaveA = kJa / kWaves;
+  constexpr int kPerWaveB = kJb / kWaves;
+  static_assert(kJa % kWaves == 0 && kJb % kWaves == 0, "DMA instructions must split evenly over waves");
+  uint32_t a_off[kPerWaveA];
+  uint32_t b_off[kPerWaveB];
+  int a_live = 0;  // A DMA instructions this wave issues per slab (masked skips empty fragments)
+  // instruction j covers tile rows 8j..8j+7; lane l fills LDS slot (l & 7) of
+  // row 8j + (l >> 3) with the global chunk that belongs there
+#pragma unroll
+  for (int jj = 0; jj < kPerWaveA; ++jj) {
+    const int j = jj * kWaves + wave;
+    const int r = 8 * j + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz(r);
+    int row = m0 + r;
+    row = row < row_limit ? row : row_limit - 1;
+    a_off[jj] = (uint32_t)row * (uint32_t)K + 16u * chunk;
+    a_live += (m0 + 8 * j < a_rows) ? 1 : 0;
+  }
+#pragma unroll
+  for (int jj = 0; jj < kPerWaveB; ++jj) {
+    const int j = jj * kWaves + wave;
+    const int r = 8 * j + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz(r);
+    int row = n0 + r;
+    row = row < p.n ? row : p.n - 1;
+    b_off[jj] = (uint32_t)row * (uint32_t)K + 16u * chunk;
+  }
+  // Row scales: BM floats, one dword instruction per 64 rows.  Every wave
+  // issues exactly one (waves past the needed count repeat a block with the
+  // same data), so every wave issues the same number of loads per slab.
+  constexpr int kSaInsts = (BM + 63) / 64;
+  const int sa_blk = wave % kSaInsts;
+  const bool sa_lane = sa_blk * 64 + lane < BM;
+  uint32_t sa_off;
+  {
+    int row = m0 + sa_blk * 64 + lane;
+    row = row < row_limit ? row : row_limit - 1;
+    sa_off = (uint32_t)row;
+  }
+  // B block scales of the 128-row blocks this tile touches (every wave)
+  const int nb0 = n0 >> 7;
+  const bool sb_lane = lane < S::kSbCount;
+  uint32_t sb_off;
+  {
+    int blk = nb0 + lane;
+    blk = blk < p.nb_count ? blk : p.nb_count - 1;
+    sb_off = (uint32_t)blk * (uint32_t)KB;
+  }
+  const int c_loads = a_live + kPerWaveB + 2;
+
   auto issue_slab = [&](int kb, int buf) {
     uint8_t* st = smem + buf * S::kStage;
+    const uint8_t* a_k = A + kb * kSlab;
+    const uint8_t* b_k = B + kb * kSlab;
 #pragma unroll
-    for (int j0 = 0; j0 < kJa + kJb; j0 += kWaves) {
-      const int j = j0 + wave;
-      if (j < kJa) {
-        const int f = j >> 1, h = j & 1;
-        if (VAR == kMasked && m0 + 16 * f >= valid_rows) continue;  // skip empty fragments
-        int row = m0 + 16 * f + (lane & 15);
-        row = row < row_limit ? row : row_limit - 1;
-        const uint8_t* src = A + (size_t)row * K + kb * kSlab + 16 * (4 * h + (lane >> 4));
-        lds_dma16(src, st + j * kFragBytes);
-      } else if (j < kJa + kJb) {
-        const int jb = j - kJa;
-        const int f = jb >> 1, h = jb & 1;
-        int row = n0 + 16 * f + (lane & 15);
-        row = row < p.n ? row : p.n - 1;
-        const uint8_t* src = B + (size_t)row * K + kb * kSlab + 16 * (4 * h + (lane >> 4));
-        lds_dma16(src, st + S::kA + jb * kFragBytes);
-      }
+    for (int jj = 0; jj < kPerWaveA; ++jj) {
+      const int j = jj * kWaves + wave;
+      if (VAR == kMasked && m0 + 8 * j >= a_rows) continue;  // rows without results
+      lds_dma16(a_k + a_off[jj], st + j * kDmaBytes);
     }
-    // row scales of this slab: BM floats, 64 per instruction
 #pragma unroll
-    for (int j0 = 0; j0 < (BM + 63) / 64; j0 += kWaves) {
-      const int j = j0 + wave;
-      if (j < (BM + 63) / 64 && j * 64 + lane < BM) {
-        int row = m0 + j * 64 + lane;
-        row = row < row_limit ? row : row_limit - 1;
-        lds_dma4(SFA + (size_t)kb * p.sfa_ld + row, st + S::kA + S::kB + j * 256);
-      }
+    for (int jj = 0; jj < kPerWaveB; ++jj) {
+      const int j = jj * kWaves + wave;
+      lds_dma16(b_k + b_off[jj], st + S::kA + j * kDmaBytes);
     }
+    if (sa_lane) lds_dma4(SFA + (size_t)kb * p.sfa_ld + sa_off, st + S::kA + S::kB + sa_blk * 256);
+    if (sb_lane) lds_dma4(SFB + sb_off + kb, st + S::kA + S::kB + S::kSa);
   };
 
   v4f acc[FM][FN];
@@ -233,80 +332,139 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // B scale rows of this wave's fragments (clamped for columns past n)
-  int sb_row[FN];
+  // index of each fragment's B scale block among the tile's blocks
+  int sb_idx[FN];
 #pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    int blk = (n0 + wn * TN + j * 16) >> 7;
-    sb_row[j] = (blk < p.nb_count ? blk : p.nb_count - 1) * KB;
-  }
+  for (int j = 0; j < FN; ++j) sb_idx[j] = ((n0 + wn * TN + j * 16) >> 7) - nb0;
+  constexpr bool kSbUniform = (128 % TN) == 0;  // a wave's columns lie in one block
   // fragments of this wave that hold at least one valid row
-  const int frag_rows0 = m0 + wm * TM;
   int fm_valid = FM;
   if (VAR == kMasked) {
-    const int left = valid_rows - frag_rows0;
+    const int left = valid_rows - (m0 + wm * TM);
     fm_valid = left <= 0 ? 0 : (left + 15) / 16;
   }
 
-  issue_slab(0, 0);
-  for (int kb = 0; kb < KB; ++kb) {
-    wait_vmem_all();
-    __syncthreads();  // slab kb is in LDS; every wave is done with slab kb-1
-    if (kb + 1 < KB) issue_slab(kb + 1, (kb + 1) & 1);
+  // per-lane LDS byte offsets of the two 16-byte chunks of a fragment read
+  // (row lane & 15 of the fragment, K chunks g and g + 4, g = lane >> 4)
+  const int fr = lane & 15;
+  const uint32_t frag_lo = (uint32_t)(fr * 128 + 16 * ((lane >> 4) ^ swz(fr)));
+  const uint32_t frag_hi = (uint32_t)(fr * 128 + 16 * ((4 + (lane >> 4)) ^ swz(fr)));
 
-    const uint8_t* st = smem + (kb & 1) * S::kStage;
+  // ---- prologue: DMA of slabs 0..NST-2
+#pragma unroll
+  for (int s0 = 0; s0 <= NST - 2; ++s0)
+    if (s0 < KB) issue_slab(s0, s0);
+
+  for (int kb = 0; kb < KB; ++kb) {
+    // slab kb's DMA must have landed (in every wave: then the barrier); the
+    // loads issued after it may stay in flight.
+    wait_vmem_dyn(c_loads * loads_ahead<NST>(kb, KB));
+    block_barrier();  // also: every wave is done with the stage about to be refilled
+    __builtin_amdgcn_sched_barrier(0);
+    if (kb + NST - 1 < KB) issue_slab(kb + NST - 1, (kb + NST - 1) % NST);
+    __builtin_amdgcn_sched_barrier(0);
+
+    const uint8_t* st = smem + (kb % NST) * S::kStage;
     const uint8_t* sA = st;
     const uint8_t* sB = st + S::kA;
     const float* sSa = (const float*)(st + S::kA + S::kB);
+    const float* sSb = (const float*)(st + S::kA + S::kB + S::kSa);
 
     float sbv[FN];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) sbv[j] = SFB[sb_row[j] + kb];
+    for (int j = 0; j < FN; ++j) sbv[j] = sSb[kSbUniform ? sb_idx[0] : sb_idx[j]];
 
     v8i bf[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int f = wn * FN + j;
-      const v4i lo = *(const v4i*)(sB + (2 * f + 0) * kFragBytes + lane * 16);
-      const v4i hi = *(const v4i*)(sB + (2 * f + 1) * kFragBytes + lane * 16);
+      const v4i lo = *(const v4i*)(sB + f * 2048 + frag_lo);
+      const v4i hi = *(const v4i*)(sB + f * 2048 + frag_hi);
       bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      if (VAR == kMasked && i >= fm_valid) continue;
+
+    // Software pipeline over the wave's FM x FN fragments (row-major order t):
+    // A rows are read from LDS kPf rows ahead, and fragment t's promotion
+    // runs kLag fragments after its MFMA, so each MFMA has independent
+    // promotion FMAs of earlier fragments to co-issue with.
+    constexpr int kPf = FM < 2 ? FM : 2;
+    constexpr int kAbuf = kPf + 1;
+    constexpr int kSabuf = kPf + 2;
+    constexpr int kLag = 2;
+    constexpr int F = FM * FN;
+    v8i abuf[kAbuf];
+    v4f sabuf[kSabuf];
+    v4f pr[kLag + 1];
+    auto load_a = [&](int i) {
       const int f = wm * FM + i;
-      const v4i lo = *(const v4i*)(sA + (2 * f + 0) * kFragBytes + lane * 16);
-      const v4i hi = *(const v4i*)(sA + (2 * f + 1) * kFragBytes + lane * 16);
-      const v8i af = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      const v4f sa = *(const v4f*)(sSa + wm * TM + i * 16 + 4 * (lane >> 4));
+      const v4i lo = *(const v4i*)(sA + f * 2048 + frag_lo);
+      const v4i hi = *(const v4i*)(sA + f * 2048 + frag_hi);
+      abuf[i % kAbuf] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      sabuf[i % kSabuf] = *(const v4f*)(sSa + wm * TM + i * 16 + 4 * (lane >> 4));
+    };
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const v4f pr = mfma_fp8_16x16x128(af, bf[j]);
-        const v4f s = sa * sbv[j];
-        acc[i][j][0] = __builtin_fmaf(pr[0], s[0], acc[i][j][0]);
-        acc[i][j][1] = __builtin_fmaf(pr[1], s[1], acc[i][j][1]);
-        acc[i][j][2] = __builtin_fmaf(pr[2], s[2], acc[i][j][2]);
-        acc[i][j][3] = __builtin_fmaf(pr[3], s[3], acc[i][j][3]);
+    for (int i = 0; i < kPf; ++i)
+      if (VAR != kMasked || i < fm_valid) load_a(i);
+#pragma unroll
+    for (int t = 0; t < F + kLag; ++t) {
+      if (t < F) {
+        const int i = t / FN, j = t % FN;
+        if (VAR != kMasked || i < fm_valid) {
+          if (j == 0 && i + kPf < FM && (VAR != kMasked || i + kPf < fm_valid)) load_a(i + kPf);
+          pr[t % (kLag + 1)] = mfma_fp8_16x16x128(abuf[i % kAbuf], bf[j]);
+        }
+      }
+      if (t >= kLag) {
+        const int u = t - kLag;
+        const int i = u / FN, j = u % FN;
+        if (VAR != kMasked || i < fm_valid) {
+          const v4f sc = sabuf[i % kSabuf] * sbv[j];
+          const v4f pv = pr[u % (kLag + 1)];
+          acc[i][j][0] = __builtin_fmaf(pv[0], sc[0], acc[i][j][0]);
+          acc[i][j][1] = __builtin_fmaf(pv[1], sc[1], acc[i][j][1]);
+          acc[i][j][2] = __builtin_fmaf(pv[2], sc[2], acc[i][j][2]);
+          acc[i][j][3] = __builtin_fmaf(pv[3], sc[3], acc[i][j][3]);
+        }
       }
     }
   }
 
-  // ---- epilogue: bf16 round-to-nearest-even, valid rows and columns only
+  // ---- epilogue: bf16 (round to nearest even) through LDS, then 16-byte
+  // coalesced row stores of valid rows and columns
+  wait_vmem_all();  // no LDS DMA may be in flight while the tile is staged
+  block_barrier();  // every wave is done reading the last stage
+  uint8_t* so = smem;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     if (VAR == kMasked && i >= fm_valid) continue;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int rl = wm * TM + i * 16 + 4 * (lane >> 4) + e;
-      const int row = m0 + rl;
-      bool ok = row < valid_rows;
-      if (VAR == kContiguous) ok = ok && s_row_ok[rl];
-      if (!ok) continue;
+    for (int j = 0; j < FN; ++j) {
+      const int cl = wn * TN + j * 16 + (lane & 15);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int col = n0 + wn * TN + j * 16 + (lane & 15);
-        if (col < p.n) D[(size_t)row * p.n + col] = f32_to_bf16_rne(acc[i][j][e]);
+      for (int e = 0; e < 4; ++e) {
+        const int rl = wm * TM + i * 16 + 4 * (lane >> 4) + e;
+        *(uint16_t*)(so + rl * S::kOutPitch + cl * 2) = f32_to_bf16_rne(acc[i][j][e]);
       }
+    }
+  }
+  block_barrier();
+  const int rows_here = min(BM, valid_rows - m0);  // rows of this tile with results
+  const int cols_here = min(BN, p.n - n0);
+  if ((p.n & 7) == 0) {
+    constexpr int kChunks = BN / 8;  // 16-byte chunks per tile row
+    for (int idx = threadIdx.x; idx < BM * kChunks; idx += kThreads) {
+      const int rl = idx / kChunks, ch = idx % kChunks;
+      if (rl >= rows_here || ch * 8 >= cols_here) continue;
+      if (VAR == kContiguous && !s_row_ok[rl]) continue;
+      const v4i v = *(const v4i*)(so + rl * S::kOutPitch + ch * 16);
+      *(v4i*)(D + (size_t)(m0 + rl) * p.n + n0 + ch * 8) = v;
+    }
+  } else {
+    for (int idx = threadIdx.x; idx < BM * BN; idx += kThreads) {
+      const int rl = idx / BN, cl = idx % BN;
+      if (rl >= rows_here || cl >= cols_here) continue;
+      if (VAR == kContiguous && !s_row_ok[rl]) continue;
+      D[(size_t)(m0 + rl) * p.n + n0 + cl] = *(const uint16_t*)(so + rl * S::kOutPitch + cl * 2);
     }
   }
 }

@@ -20,7 +20,8 @@ from tests import gpu_harness as H
 
 pytestmark = pytest.mark.gpu
 
-DENSE_CONFIGS = ["dense_256x256_w8", "dense_128x128_w4", "dense_64x64_w4"]
+DENSE_CONFIGS = ["dense_256x256_w8_s2", "dense_256x128_w8_s3", "dense_128x256_w8_s3", "dense_128x128_w4_s3",
+                 "dense_128x128_w4_s2", "dense_64x64_w4_s3"]
 
 
 def dense_case(m, n, k, seed, b_std=1.0):
@@ -79,7 +80,7 @@ def test_dense_unit_scale_exact_values(gpu):
     assert np.all(H.d_float(d) == k)
 
 
-@pytest.mark.parametrize("cfg", [None, "contig_128x256_w8", "contig_128x128_w4"])
+@pytest.mark.parametrize("cfg", [None, "contig_128x256_w8_s3", "contig_128x128_w4_s3"])
 def test_contiguous(gpu, cfg, monkeypatch):
     if cfg:
         monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
@@ -102,8 +103,8 @@ def test_contiguous(gpu, cfg, monkeypatch):
     assert H.guard_untouched(flat, d.numel())
 
 
-@pytest.mark.parametrize("cfg,max_m", [(None, 96), (None, 256), ("masked_256x128_w4", 300),
-                                       ("masked_64x64_w4", 130)])
+@pytest.mark.parametrize("cfg,max_m", [(None, 96), (None, 256), ("masked_256x128_w4_s2", 300),
+                                       ("masked_256x128_w4_s3", 200), ("masked_64x64_w4_s3", 130)])
 def test_masked(gpu, cfg, max_m, monkeypatch):
     if cfg:
         monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
@@ -124,3 +125,23 @@ def test_masked(gpu, cfg, max_m, monkeypatch):
     bits = H.d_bits(d)
     assert np.all(bits[~valid] == H.SENTINEL)
     assert H.guard_untouched(flat, d.numel())
+
+
+def test_unknown_forced_config_is_an_error(gpu, monkeypatch):
+    monkeypatch.setenv("DG_FORCE_CONFIG", "no_such_config")
+    qa, sa, qb, sb = dense_case(64, 64, 128, seed=1)
+    with pytest.raises(Exception, match="DG_FORCE_CONFIG"):
+        H.run_dense(qa, sa, qb, sb, gpu)
+
+
+def test_dense_long_k_pipeline(gpu):
+    # many slabs: the prologue, the steady state and the drain of the load pipeline
+    for cfg in DENSE_CONFIGS:
+        import os
+        os.environ["DG_FORCE_CONFIG"] = cfg
+        try:
+            check_dense(gpu, *dense_case(136, 264, 128 * 13, seed=5), label=f"{cfg} long k")
+            check_dense(gpu, *dense_case(136, 264, 128 * 2, seed=6), label=f"{cfg} k=256")
+            check_dense(gpu, *dense_case(136, 264, 128, seed=7), label=f"{cfg} k=128")
+        finally:
+            del os.environ["DG_FORCE_CONFIG"]
