@@ -26,6 +26,7 @@ __all__ = [
     "DGError", "lib", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous",
     "m_grouped_fp8_gemm_nt_masked", "quantize_a_1x128", "quantize_b_128x128",
     "get_m_alignment_for_contiguous_layout", "get_sfa_ld", "empty_sfa", "profile_next_launch",
+    "reserve_workspace",
 ]
 
 
@@ -51,6 +52,7 @@ _SIGNATURES = {
     "dg_last_error_message": [],
     "dg_version": [],
     "dg_profile_next_launch": [_vp, _vp],
+    "dg_reserve_workspace": [ctypes.c_size_t],
 }
 _RESTYPES = {"dg_status_string": ctypes.c_char_p, "dg_last_error_message": ctypes.c_char_p,
              "dg_version": ctypes.c_char_p}
@@ -106,6 +108,11 @@ def profile_next_launch(start_event, stop_event):
     objects (timing enabled, already recorded once so they exist) at the start
     and end of the kernel itself."""
     _check(lib().dg_profile_next_launch(start_event._as_parameter_, stop_event._as_parameter_))
+
+
+def reserve_workspace(nbytes):
+    """Pre-allocate the split-K workspace on the current device."""
+    _check(lib().dg_reserve_workspace(int(nbytes)))
 
 
 def get_m_alignment_for_contiguous_layout():

@@ -111,6 +111,8 @@ const Config* configs(int* count) {
       make_config<128, 128, 2, 2, 3, dg::kDense>("dense_128x128_w4_s3"),
       make_config<128, 128, 2, 2, 2, dg::kDense>("dense_128x128_w4_s2"),
       make_config<64, 64, 1, 4, 3, dg::kDense>("dense_64x64_w4_s3"),
+      // skinny M: split-K over workgroups, up to 7 slabs of a split in flight
+      make_config<64, 64, 1, 4, 8, dg::kDense>("dense_64x64_w4_s8"),
       // contiguous (block rows <= the 128-row alignment)
       make_config<128, 256, 2, 4, 3, dg::kContiguous>("contig_128x256_w8_s3"),
       make_config<128, 128, 2, 2, 3, dg::kContiguous>("contig_128x128_w4_s3"),
@@ -156,6 +158,42 @@ void set_kernel_attributes() {
     hipError_t e = hipFuncSetAttribute(t[i].fn, hipFuncAttributeMaxDynamicSharedMemorySize, t[i].smem);
     if (e != hipSuccess) g_attr_err = e;
   }
+}
+
+// ---- split-K workspace: library-owned device memory per device, grown on
+// demand.  Layout: kCounterInts arrival counters (zeroed once, reset by the
+// kernels), then the fp32 partial tiles.
+constexpr size_t kCounterInts = 1 << 16;
+struct Workspace {
+  std::mutex mu;
+  char* base = nullptr;
+  size_t bytes = 0;
+};
+Workspace g_ws[kMaxDevices];
+
+int ensure_workspace(int dev, size_t partial_bytes, float** partial, int** counters) {
+  Workspace& w = g_ws[dev];
+  std::lock_guard<std::mutex> lock(w.mu);
+  const size_t need = kCounterInts * sizeof(int) + partial_bytes;
+  if (w.bytes < need) {
+    if (w.base) {
+      hipError_t e = hipFree(w.base);  // synchronises the device
+      w.base = nullptr;
+      w.bytes = 0;
+      if (e != hipSuccess) return fail(DG_ERR_HIP, "hipFree(workspace): %s", hipGetErrorString(e));
+    }
+    size_t alloc = need < ((size_t)16 << 20) ? ((size_t)16 << 20) : need;
+    void* ptr = nullptr;
+    hipError_t e = hipMalloc(&ptr, alloc);
+    if (e != hipSuccess) return fail(DG_ERR_HIP, "hipMalloc(workspace %zu): %s", alloc, hipGetErrorString(e));
+    e = hipMemset(ptr, 0, kCounterInts * sizeof(int));
+    if (e != hipSuccess) return fail(DG_ERR_HIP, "hipMemset(workspace): %s", hipGetErrorString(e));
+    w.base = (char*)ptr;
+    w.bytes = alloc;
+  }
+  *counters = (int*)w.base;
+  *partial = (float*)(w.base + kCounterInts * sizeof(int));
+  return DG_OK;
 }
 
 int launch(const Config& c, dg::GemmParams& p, int grid, hipStream_t stream) {
@@ -218,6 +256,16 @@ int dg_get_sfa_ld(int m) { return m < 0 ? 0 : sfa_ld(m); }
 
 const char* dg_version(void) { return "dg-gfx950 0.1"; }
 
+int dg_reserve_workspace(size_t bytes) {
+  int dev;
+  DeviceInfo* info;
+  if (int s = current_device(&dev, &info)) return s;
+  float* part;
+  int* cnt;
+  if (int s = ensure_workspace(dev, bytes, &part, &cnt)) return s;
+  return ok();
+}
+
 int dg_profile_next_launch(void* start_event, void* stop_event) {
   g_prof_start = (hipEvent_t)start_event;
   g_prof_stop = (hipEvent_t)stop_event;
@@ -254,8 +302,8 @@ int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const f
   const Config* c;
   if (int s = forced_config(dg::kDense, &c)) return s;
   if (!c) {
-    if (m <= 64) c = find_config("dense_64x64_w4_s3", dg::kDense);
-    else if (m <= 256 || n <= 256) c = find_config("dense_128x128_w4_s3", dg::kDense);
+    if (m <= 64) c = find_config("dense_64x64_w4_s8", dg::kDense);
+    else if (m <= 256 || n <= 256) c = find_config("dense_128x128_w4_s2", dg::kDense);
     else c = find_config("dense_256x256_w8_s2", dg::kDense);
   }
   dg::GemmParams p{};
@@ -263,7 +311,32 @@ int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const f
   p.num_groups = 1;
   fill_common(p, *c, m, n, k);
   p.num_tiles = p.tiles_m * p.tiles_n;
-  return launch(*c, p, p.num_tiles, (hipStream_t)stream);
+  p.splits = 1;
+  p.split_slabs = p.kb_count;
+  // Split K over workgroups when the tiles alone cannot fill the GPU (skinny
+  // M): one wave of workgroups, each with at most NST-1 slabs so that all of
+  // its loads are in flight at once.
+  int splits = 1;
+  if (const char* e = getenv("DG_SPLIT_K")) splits = atoi(e);
+  else if (p.num_tiles * 2 <= info->cus && p.kb_count >= 4) {
+    splits = info->cus / p.num_tiles;
+    const int min_split_slabs = 2;
+    if (splits > p.kb_count / min_split_slabs) splits = p.kb_count / min_split_slabs;
+    if (splits > 8) splits = 8;  // the reducer reads up to 8 partials per batch
+  }
+  if (splits > 1) {
+    const int per = (p.kb_count + splits - 1) / splits;
+    splits = (p.kb_count + per - 1) / per;  // no empty splits
+    p.splits = splits;
+    p.split_slabs = per;
+  }
+  if (p.splits > 1) {
+    if ((size_t)p.num_tiles > kCounterInts)
+      return fail(DG_ERR_UNSUPPORTED_SHAPE, "too many tiles for split-K (%d)", p.num_tiles);
+    const size_t part = (size_t)p.num_tiles * p.splits * c->bm * c->bn * sizeof(float);
+    if (int s = ensure_workspace(dev, part, &p.ws_partial, &p.ws_count)) return s;
+  }
+  return launch(*c, p, p.num_tiles * p.splits, (hipStream_t)stream);
 }
 
 int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b,

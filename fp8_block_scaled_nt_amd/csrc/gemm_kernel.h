@@ -48,7 +48,11 @@ enum Variant { kDense = 0, kContiguous = 1, kMasked = 2 };
 
 constexpr int kSlab = 128;        // K bytes per slab (one scale per slab)
 constexpr int kNumXcd = 8;        // MI355X: 8 XCDs, workgroups dealt round-robin
-constexpr int kDmaBytes = 1024;   // LDS bytes one wave-wide 16-byte-per-lane DMA writes
+constexpr int kDmaBytes = 1024;
+// Word 3 of a raw buffer resource for gfx9 (32-bit data format; offsets past
+// num_records read as zero) and the SC1 cache-policy bit of buffer accesses.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kCpolSc1 = 16;   // LDS bytes one wave-wide 16-byte-per-lane DMA writes
 
 struct GemmParams {
   const uint8_t* a;
@@ -69,6 +73,13 @@ struct GemmParams {
   int tiles_n;
   int num_tiles;
   int group_m;               // raster group height in tiles
+  // split-K (dense): each tile's K slabs are shared by `splits` workgroups of
+  // `split_slabs` slabs each; their fp32 partial tiles meet in a workspace and
+  // the last workgroup to arrive adds them in split order and stores D.
+  int splits;
+  int split_slabs;
+  float* ws_partial;         // [num_tiles][splits][BM * BN] fp32, fragment-native order
+  int* ws_count;             // [num_tiles] arrival counters, zero between calls
 };
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -192,7 +203,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   static_assert(NST >= 2, "pipeline shape");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ int s_expert;
+  __shared__ int s_flag;  // contiguous: block expert; split-K: last-arriver flag
   __shared__ uint8_t s_row_ok[BM];
 
   const int lane = threadIdx.x & 63;
@@ -200,8 +211,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   const int wm = wave / WN;
   const int wn = wave % WN;
 
-  // ---- tile -> (group, tile_m, tile_n)
-  int g = 0, tm, tn;
+  // ---- tile -> (group, tile_m, tile_n[, split])
+  int g = 0, tm, tn, tile_id = 0, split = 0;
   if (VAR == kMasked) {
     const int t = blockIdx.x;
     const int per_g = p.tiles_m * p.tiles_n;
@@ -209,6 +220,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
     const int r = t - g * per_g;
     tm = r / p.tiles_n;
     tn = r - tm * p.tiles_n;
+  } else if (p.splits > 1) {
+    tile_id = blockIdx.x / p.splits;
+    split = blockIdx.x - tile_id * p.splits;
+    tm = tile_id / p.tiles_n;
+    tn = tile_id - tm * p.tiles_n;
   } else {
     const int t = xcd_remap(blockIdx.x, gridDim.x);
     raster(t, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
@@ -225,15 +241,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   const int row_limit = p.m;  // rows that exist in memory (load clamp)
   int valid_rows = p.m;       // rows with a result (masked: the expert's count)
   if (VAR == kContiguous) {
-    if (threadIdx.x == 0) s_expert = -1;
+    if (threadIdx.x == 0) s_flag = -1;
     __syncthreads();
     int tag = -1;
     if (threadIdx.x < BM) {
       tag = p.m_indices[m0 + threadIdx.x];
-      if (tag >= 0 && tag < p.num_groups) atomicMax(&s_expert, tag);
+      if (tag >= 0 && tag < p.num_groups) atomicMax(&s_flag, tag);
     }
     __syncthreads();
-    const int expert = s_expert;
+    const int expert = s_flag;
     if (expert < 0) return;  // a block of padding rows only
     if (threadIdx.x < BM) s_row_ok[threadIdx.x] = (tag == expert);
     B += (size_t)expert * p.n * p.k;
@@ -249,7 +265,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
     SFB += (size_t)g * p.nb_count * p.kb_count;
     D += (size_t)g * p.m * p.n;
   }
-  const int KB = p.kb_count;
+  // K slabs of this workgroup: [kb0, kb0 + KB) (KB is local; p.kb_count is K/128)
+  const int kb0 = split * p.split_slabs;
+  const int KB = p.splits > 1 ? min(p.split_slabs, p.kb_count - kb0) : p.kb_count;
   const int K = p.k;
   // rows worth loading: the masked layout never reads rows past the count
   const int a_rows = VAR == kMasked ? valid_rows : row_limit;
@@ -303,11 +321,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   {
     int blk = nb0 + lane;
     blk = blk < p.nb_count ? blk : p.nb_count - 1;
-    sb_off = (uint32_t)blk * (uint32_t)KB;
+    sb_off = (uint32_t)blk * (uint32_t)p.kb_count;  // sfb row stride: all K slabs
   }
   const int c_loads = a_live + kPerWaveB + 2;
 
-  auto issue_slab = [&](int kb, int buf) {
+  auto issue_slab = [&](int kl, int buf) {
+    const int kb = kb0 + kl;  // global slab index
     uint8_t* st = smem + buf * S::kStage;
     const uint8_t* a_k = A + kb * kSlab;
     const uint8_t* b_k = B + kb * kSlab;
@@ -429,9 +448,62 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
     }
   }
 
+  wait_vmem_all();  // no LDS DMA may be in flight past this point
+
+  // ---- split-K fix-up: publish this split's partial tile; the last split
+  // to arrive adds all partials in split order (deterministic) and goes on to
+  // store D.  Partials are laid out fragment-native (each lane owns 16
+  // contiguous bytes per fragment) and move with SC1 buffer stores and loads,
+  // which are coherent across the per-XCD L2s (the agent-scope path), so no
+  // L2 write-back or invalidate is needed.  The reducer reads kChunk splits'
+  // partials per batch; loads past the last split return zero.
+  if (VAR == kDense && p.splits > 1) {
+    constexpr int kTileFloats = BM * BN;
+    constexpr int kChunk = (FM * FN * 4) >= 128 ? 1 : 128 / (FM * FN * 4);
+    float* part = p.ws_partial + (size_t)tile_id * p.splits * kTileFloats;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(part, 0, p.splits * kTileFloats * 4, kBufferRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            acc[i][j], rs, (split * kTileFloats + (((wave * FM + i) * FN + j) * 64 + lane) * 4) * 4, 0, kCpolSc1);
+    wait_vmem_all();  // this thread's partial stores are complete (in memory)
+    __syncthreads();  // ... and so are every other thread's
+    if (threadIdx.x == 0) {
+      const int arrived = __hip_atomic_fetch_add(p.ws_count + tile_id, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_flag = (arrived == p.splits - 1) ? 1 : 0;
+    }
+    __syncthreads();
+    if (s_flag == 0) return;  // not the last split: done
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int sp0 = 0; sp0 < p.splits; sp0 += kChunk) {
+      v4f part_v[kChunk][FM][FN];
+#pragma unroll
+      for (int c = 0; c < kChunk; ++c)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            part_v[c][i][j] = __builtin_amdgcn_raw_buffer_load_b128(
+                rs, ((sp0 + c) * kTileFloats + (((wave * FM + i) * FN + j) * 64 + lane) * 4) * 4, 0, kCpolSc1);
+#pragma unroll
+      for (int c = 0; c < kChunk; ++c)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] += part_v[c][i][j];
+    }
+    if (threadIdx.x == 0)  // ready for the next call
+      __hip_atomic_store(p.ws_count + tile_id, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
   // ---- epilogue: bf16 (round to nearest even) through LDS, then 16-byte
   // coalesced row stores of valid rows and columns
-  wait_vmem_all();  // no LDS DMA may be in flight while the tile is staged
   block_barrier();  // every wave is done reading the last stage
   uint8_t* so = smem;
 #pragma unroll

@@ -45,6 +45,7 @@
 #ifndef DG_H
 #define DG_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -67,7 +68,13 @@ typedef enum {
  * Dense FP8 NT GEMM: D[m][n] = A[m][k] . B[n][k]^T with 1x128 (A) and
  * 128x128 (B) fp32 block scales.  Rows m and columns n may be any size >= 0
  * and >= 1 respectively; a partial last 128-row block of B uses its own scale
- * row of sfb.
+ * row of sfb.  When the output tiles alone cannot fill the GPU (skinny m),
+ * the K dimension is split over several workgroups whose fp32 partial tiles
+ * meet in a library-owned device workspace and are added in a fixed order,
+ * so results stay bit-for-bit reproducible.  The workspace is allocated (or
+ * grown) by the first call that needs it on a device; that call is then not
+ * graph-capturable (dg_reserve_workspace avoids this), and concurrent
+ * split-K calls on one device must not overlap in time.
  */
 int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
                    uint16_t* d, int m, int n, int k, dg_stream_t stream);
@@ -124,6 +131,14 @@ int dg_quantize_a_1x128(const float* x, uint8_t* q, float* sfa, int m, int k, dg
  * the last row block may be partial.
  */
 int dg_quantize_b_128x128(const float* x, uint8_t* q, float* sfb, int n, int k, dg_stream_t stream);
+
+/*
+ * Pre-allocate the split-K workspace of the current device with room for
+ * `bytes` of partial tiles (a tile of BM x BN outputs takes 4*BM*BN bytes per
+ * split).  Calls that then fit allocate nothing.  Synchronises the device
+ * when it has to grow the workspace.
+ */
+int dg_reserve_workspace(size_t bytes);
 
 /* Static text for a status code. */
 const char* dg_status_string(int status);

@@ -145,3 +145,29 @@ def test_dense_long_k_pipeline(gpu):
             check_dense(gpu, *dense_case(136, 264, 128, seed=7), label=f"{cfg} k=128")
         finally:
             del os.environ["DG_FORCE_CONFIG"]
+
+
+@pytest.mark.parametrize("m,n,k,splits", [
+    (64, 2112, 7168, None),   # the decode shape, default split choice
+    (17, 200, 1280, "3"),     # 10 slabs over 3 splits: 4 + 4 + 2
+    (1, 64, 512, "4"),
+    (64, 130, 896, "7"),      # one slab per split
+    (100, 192, 768, "2"),     # two tile rows
+])
+def test_dense_split_k(gpu, m, n, k, splits, monkeypatch):
+    if splits:
+        monkeypatch.setenv("DG_SPLIT_K", splits)
+    monkeypatch.setenv("DG_FORCE_CONFIG", "dense_64x64_w4_s8")
+    qa, sa, qb, sb = dense_case(m, n, k, seed=m * 3 + k, b_std=0.02)
+    d = check_dense(gpu, qa, sa, qb, sb, label=f"split-K {m}x{n}x{k} splits={splits}")
+    # bit-for-bit reproducible, and the arrival counters are reset for the next call
+    d2, _ = H.run_dense(qa, sa, qb, sb, gpu)
+    assert np.array_equal(H.d_bits(d), H.d_bits(d2))
+
+
+def test_split_k_back_to_back_shapes(gpu, monkeypatch):
+    # calls with different split counts and tile counts in a row share the workspace
+    monkeypatch.setenv("DG_FORCE_CONFIG", "dense_64x64_w4_s8")
+    for splits, (m, n, k) in [("5", (64, 512, 1280)), ("2", (40, 1024, 512)), ("7", (64, 512, 1792))]:
+        monkeypatch.setenv("DG_SPLIT_K", splits)
+        check_dense(gpu, *dense_case(m, n, k, seed=11), label=f"back-to-back splits={splits}")
