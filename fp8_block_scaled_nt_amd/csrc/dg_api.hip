@@ -107,6 +107,9 @@ const Config* configs(int* count) {
       // dense
       make_config<256, 256, 2, 4, 2, dg::kDense>("dense_256x256_w8_s2"),
       make_config<256, 128, 4, 2, 3, dg::kDense>("dense_256x128_w8_s3"),
+      make_config<256, 128, 2, 2, 2, dg::kDense>("dense_256x128_w4_s2"),
+      make_config<256, 128, 2, 2, 3, dg::kDense>("dense_256x128_w4_s3"),
+      make_config<128, 256, 2, 2, 3, dg::kDense>("dense_128x256_w4_s3"),
       make_config<128, 256, 2, 4, 3, dg::kDense>("dense_128x256_w8_s3"),
       make_config<128, 128, 2, 2, 3, dg::kDense>("dense_128x128_w4_s3"),
       make_config<128, 128, 2, 2, 2, dg::kDense>("dense_128x128_w4_s2"),
@@ -116,7 +119,10 @@ const Config* configs(int* count) {
       // contiguous (block rows <= the 128-row alignment)
       make_config<128, 256, 2, 4, 3, dg::kContiguous>("contig_128x256_w8_s3"),
       make_config<128, 128, 2, 2, 3, dg::kContiguous>("contig_128x128_w4_s3"),
+      make_config<128, 128, 2, 2, 2, dg::kContiguous>("contig_128x128_w4_s2"),
+      make_config<128, 256, 2, 4, 2, dg::kContiguous>("contig_128x256_w8_s2"),
       // masked
+      make_config<256, 256, 2, 4, 2, dg::kMasked>("masked_256x256_w8_s2"),
       make_config<256, 128, 1, 4, 2, dg::kMasked>("masked_256x128_w4_s2"),
       make_config<256, 128, 1, 4, 3, dg::kMasked>("masked_256x128_w4_s3"),
       make_config<64, 64, 1, 4, 3, dg::kMasked>("masked_64x64_w4_s3"),
@@ -359,7 +365,7 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, cons
   if (int s = current_device(&dev, &info)) return s;
   const Config* c;
   if (int s = forced_config(dg::kContiguous, &c)) return s;
-  if (!c) c = find_config(n >= 256 ? "contig_128x256_w8_s3" : "contig_128x128_w4_s3", dg::kContiguous);
+  if (!c) c = find_config("contig_128x128_w4_s2", dg::kContiguous);
   dg::GemmParams p{};
   p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.m_indices = m_indices;
   p.num_groups = num_groups;
@@ -388,7 +394,7 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const ui
   if (int s = current_device(&dev, &info)) return s;
   const Config* c;
   if (int s = forced_config(dg::kMasked, &c)) return s;
-  if (!c) c = find_config(max_m <= 64 ? "masked_64x64_w4_s3" : "masked_256x128_w4_s2", dg::kMasked);
+  if (!c) c = find_config(max_m <= 64 ? "masked_64x64_w4_s3" : "masked_256x256_w8_s2", dg::kMasked);
   dg::GemmParams p{};
   p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.masked_m = masked_m;
   p.num_groups = num_groups;

@@ -214,7 +214,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   // ---- tile -> (group, tile_m, tile_n[, split])
   int g = 0, tm, tn, tile_id = 0, split = 0;
   if (VAR == kMasked) {
-    const int t = blockIdx.x;
+    // an expert's tiles are consecutive, and the XCD remap keeps consecutive
+    // tiles on one XCD: the expert's A rows are fetched into one L2 only
+    const int t = xcd_remap(blockIdx.x, gridDim.x);
     const int per_g = p.tiles_m * p.tiles_n;
     g = t / per_g;
     const int r = t - g * per_g;

@@ -21,7 +21,8 @@ from tests import gpu_harness as H
 pytestmark = pytest.mark.gpu
 
 DENSE_CONFIGS = ["dense_256x256_w8_s2", "dense_256x128_w8_s3", "dense_128x256_w8_s3", "dense_128x128_w4_s3",
-                 "dense_128x128_w4_s2", "dense_64x64_w4_s3"]
+                 "dense_128x128_w4_s2", "dense_64x64_w4_s3", "dense_64x64_w4_s8", "dense_256x128_w4_s2",
+                 "dense_256x128_w4_s3", "dense_128x256_w4_s3"]
 
 
 def dense_case(m, n, k, seed, b_std=1.0):
@@ -80,7 +81,8 @@ def test_dense_unit_scale_exact_values(gpu):
     assert np.all(H.d_float(d) == k)
 
 
-@pytest.mark.parametrize("cfg", [None, "contig_128x256_w8_s3", "contig_128x128_w4_s3"])
+@pytest.mark.parametrize("cfg", [None, "contig_128x256_w8_s3", "contig_128x128_w4_s3", "contig_128x128_w4_s2",
+                                 "contig_128x256_w8_s2"])
 def test_contiguous(gpu, cfg, monkeypatch):
     if cfg:
         monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
@@ -104,7 +106,8 @@ def test_contiguous(gpu, cfg, monkeypatch):
 
 
 @pytest.mark.parametrize("cfg,max_m", [(None, 96), (None, 256), ("masked_256x128_w4_s2", 300),
-                                       ("masked_256x128_w4_s3", 200), ("masked_64x64_w4_s3", 130)])
+                                       ("masked_256x128_w4_s3", 200), ("masked_64x64_w4_s3", 130),
+                                       ("masked_256x256_w8_s2", 300)])
 def test_masked(gpu, cfg, max_m, monkeypatch):
     if cfg:
         monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
