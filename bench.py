@@ -36,6 +36,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
 ROTATE_BYTES = 600 << 20       # > 2x the 256 MiB Infinity Cache
 MAIN_WORKLOAD = "dense_decode_64x2112x7168"
+CALIB_BYTES = 1 << 30          # plain-kernel traffic for the counter calibration
 METRIC = "FP8 block-scaled GEMM TFLOPS (large) & HBM GB/s (decode) on 1 GPU; % of roofline"
 
 
@@ -50,6 +51,10 @@ def parse():
                     help="'all', 'main', or a comma list of workload names for the extra figures")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--mode", choices=["bench", "counters"], default="bench",
+                    help="counters: run plain kernels of known traffic (1 GiB fill, 1 GiB read; "
+                         "calibration for rocprofv3 FETCH_SIZE/WRITE_SIZE) and eager GEMM launches "
+                         "of the headline workload, print nothing")
     return ap.parse_args()
 
 
@@ -222,6 +227,20 @@ def main():
 
     # ---- headline step: quantise A + GEMM on the decode shape
     kind, params, rot, launch, quant, inp = setup_workload(torch, np, dg, W, MAIN_WORKLOAD, dev)
+    if args.mode == "counters":
+        # plain kernels of known traffic: fill (writes CALIB_BYTES), a second fill
+        # that evicts the first from the Infinity Cache, then a sum that reads
+        # CALIB_BYTES from HBM
+        x = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+        y = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        float(x.sum())
+        del x, y
+        torch.cuda.synchronize()
+        for i in range(args.kernel_launches):
+            launch(rot[i])
+        torch.cuda.synchronize()
+        return 0
     m, n, k = params["m"], params["n"], params["k"]
     flops, gemm_bytes = W.algorithmic_work("dense", m=m, n=n, k=k)
     quant_bytes = m * k * 4 + m * k + 4 * m * (k // 128)
