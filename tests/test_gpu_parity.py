@@ -21,7 +21,7 @@ from tests import gpu_harness as H
 pytestmark = pytest.mark.gpu
 
 DENSE_CONFIGS = ["dense_256x256_w8_s2", "dense_256x128_w8_s3", "dense_128x256_w8_s3", "dense_128x128_w4_s3",
-                 "dense_128x128_w4_s2", "dense_64x64_w4_s3", "dense_64x64_w4_s8", "dense_256x128_w4_s2",
+                 "dense_128x128_w4_s2", "dense_64x64_w4_s3", "dense_64x64_w4_s8", "dense_64x32_w4_s4", "dense_256x128_w4_s2",
                  "dense_256x128_w4_s3", "dense_128x256_w4_s3"]
 
 
@@ -157,20 +157,22 @@ def test_dense_long_k_pipeline(gpu):
     (64, 130, 896, "7"),      # one slab per split
     (100, 192, 768, "2"),     # two tile rows
 ])
-def test_dense_split_k(gpu, m, n, k, splits, monkeypatch):
+@pytest.mark.parametrize("cfg", ["dense_64x64_w4_s8", "dense_64x32_w4_s4"])
+def test_dense_split_k(gpu, m, n, k, splits, cfg, monkeypatch):
     if splits:
         monkeypatch.setenv("DG_SPLIT_K", splits)
-    monkeypatch.setenv("DG_FORCE_CONFIG", "dense_64x64_w4_s8")
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
     qa, sa, qb, sb = dense_case(m, n, k, seed=m * 3 + k, b_std=0.02)
-    d = check_dense(gpu, qa, sa, qb, sb, label=f"split-K {m}x{n}x{k} splits={splits}")
+    d = check_dense(gpu, qa, sa, qb, sb, label=f"split-K {cfg} {m}x{n}x{k} splits={splits}")
     # bit-for-bit reproducible, and the arrival counters are reset for the next call
     d2, _ = H.run_dense(qa, sa, qb, sb, gpu)
     assert np.array_equal(H.d_bits(d), H.d_bits(d2))
 
 
-def test_split_k_back_to_back_shapes(gpu, monkeypatch):
+@pytest.mark.parametrize("cfg", ["dense_64x64_w4_s8", "dense_64x32_w4_s4"])
+def test_split_k_back_to_back_shapes(gpu, cfg, monkeypatch):
     # calls with different split counts and tile counts in a row share the workspace
-    monkeypatch.setenv("DG_FORCE_CONFIG", "dense_64x64_w4_s8")
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
     for splits, (m, n, k) in [("5", (64, 512, 1280)), ("2", (40, 1024, 512)), ("7", (64, 512, 1792))]:
         monkeypatch.setenv("DG_SPLIT_K", splits)
         check_dense(gpu, *dense_case(m, n, k, seed=11), label=f"back-to-back splits={splits}")
