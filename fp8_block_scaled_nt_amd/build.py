@@ -19,7 +19,7 @@ SOURCES = ["dg_api.hip"]
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
-    "-std=c++17",
+    "-std=c++20",
     "-fPIC",
     "-shared",
     # keep the compiler from forming packed fp32 VALU ops

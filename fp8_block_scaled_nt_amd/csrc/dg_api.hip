@@ -89,16 +89,16 @@ int current_device(int* dev, DeviceInfo** info) {
 // ---- tile configurations (compile-time instantiations; the host picks one)
 struct Config {
   const char* name;
-  int variant, bm, bn, wm, wn, nst;
+  int variant, bm, bn, wm, wn, nst, sched;
   const void* fn;
   int smem;
   int threads() const { return wm * wn * 64; }
 };
 
-template <int BM, int BN, int WM, int WN, int NST, int VAR>
+template <int BM, int BN, int WM, int WN, int NST, int VAR, int SCHED = dg::kInterleaved>
 Config make_config(const char* name) {
-  return Config{name, VAR, BM, BN, WM, WN, NST,
-                reinterpret_cast<const void*>(&dg::gemm_fp8_nt_kernel<BM, BN, WM, WN, NST, VAR>),
+  return Config{name, VAR, BM, BN, WM, WN, NST, SCHED,
+                reinterpret_cast<const void*>(&dg::gemm_fp8_nt_kernel<BM, BN, WM, WN, NST, VAR, SCHED>),
                 dg::Smem<BM, BN, NST>::kBytes};
 }
 
@@ -106,6 +106,9 @@ const Config* configs(int* count) {
   static const Config table[] = {
       // dense
       make_config<256, 256, 2, 4, 2, dg::kDense>("dense_256x256_w8_s2"),
+      make_config<256, 256, 2, 4, 2, dg::kDense, dg::kPingPong>("dense_256x256_w8_s2_pp"),
+      make_config<256, 224, 4, 2, 2, dg::kDense>("dense_256x224_w8_s2"),
+      make_config<128, 256, 1, 4, 3, dg::kDense>("dense_128x256_w4_s3_wide"),
       make_config<256, 128, 4, 2, 3, dg::kDense>("dense_256x128_w8_s3"),
       make_config<256, 128, 2, 2, 2, dg::kDense>("dense_256x128_w4_s2"),
       make_config<256, 128, 2, 2, 3, dg::kDense>("dense_256x128_w4_s3"),
@@ -122,8 +125,12 @@ const Config* configs(int* count) {
       make_config<128, 128, 2, 2, 3, dg::kContiguous>("contig_128x128_w4_s3"),
       make_config<128, 128, 2, 2, 2, dg::kContiguous>("contig_128x128_w4_s2"),
       make_config<128, 256, 2, 4, 2, dg::kContiguous>("contig_128x256_w8_s2"),
+      make_config<128, 256, 1, 4, 3, dg::kContiguous>("contig_128x256_w4_s3"),
+      make_config<128, 256, 1, 4, 2, dg::kContiguous>("contig_128x256_w4_s2"),
       // masked
       make_config<256, 256, 2, 4, 2, dg::kMasked>("masked_256x256_w8_s2"),
+      make_config<256, 256, 2, 4, 2, dg::kMasked, dg::kPingPong>("masked_256x256_w8_s2_pp"),
+      make_config<256, 128, 4, 2, 2, dg::kMasked>("masked_256x128_w8_s2"),
       make_config<256, 128, 1, 4, 2, dg::kMasked>("masked_256x128_w4_s2"),
       make_config<256, 128, 1, 4, 3, dg::kMasked>("masked_256x128_w4_s3"),
       make_config<64, 64, 1, 4, 3, dg::kMasked>("masked_64x64_w4_s3"),
@@ -327,7 +334,7 @@ int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const f
   // splits of 64 x 32 tiles beat one workgroup per CU by ~15%.
   int splits = 1;
   if (const char* e = getenv("DG_SPLIT_K")) splits = atoi(e);
-  else if (p.num_tiles * 2 <= info->cus && p.kb_count >= 4) {
+  else if (c->sched == dg::kInterleaved && p.num_tiles * 2 <= info->cus && p.kb_count >= 4) {
     splits = 2 * info->cus / p.num_tiles - 1;
     const int min_split_slabs = 2;
     if (splits > p.kb_count / min_split_slabs) splits = p.kb_count / min_split_slabs;
@@ -340,6 +347,8 @@ int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const f
     p.split_slabs = per;
   }
   if (p.splits > 1) {
+    if (c->sched != dg::kInterleaved)
+      return fail(DG_ERR_INVALID_ARGUMENT, "configuration %s does not support split-K", c->name);
     if ((size_t)p.num_tiles > kCounterInts)
       return fail(DG_ERR_UNSUPPORTED_SHAPE, "too many tiles for split-K (%d)", p.num_tiles);
     const size_t part = (size_t)p.num_tiles * p.splits * c->bm * c->bn * sizeof(float);
@@ -397,7 +406,7 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const ui
   if (int s = current_device(&dev, &info)) return s;
   const Config* c;
   if (int s = forced_config(dg::kMasked, &c)) return s;
-  if (!c) c = find_config(max_m <= 64 ? "masked_64x64_w4_s3" : "masked_256x256_w8_s2", dg::kMasked);
+  if (!c) c = find_config(max_m <= 64 ? "masked_64x64_w4_s3" : "masked_256x256_w8_s2_pp", dg::kMasked);
   dg::GemmParams p{};
   p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.masked_m = masked_m;
   p.num_groups = num_groups;

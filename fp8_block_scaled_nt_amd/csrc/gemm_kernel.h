@@ -36,6 +36,9 @@
 #include <hip/hip_bf16.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace dg {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -86,12 +89,45 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return __bfloat16_as_ushort(__float2bfloat16(f));
 }
 
-__device__ __forceinline__ void lds_dma16(const void* src, void* lds_dst) {
-  __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)lds_dst, 16, 0, 0);
+// Direct global -> LDS copies (LDS DMA), buffer form: each lane's 16 (or 4)
+// bytes at base + voffset + soffset land at M0 + lane * 16 (or 4).  The base
+// and the byte size of the operand sit in a wave-uniform buffer descriptor,
+// so a lane keeps only a 32-bit offset, the K slab goes into the scalar
+// offset, and a read past the operand's size returns zeros instead of
+// faulting.  They are issued from inline asm on purpose: the compiler cannot
+// tell which LDS bytes an LDS DMA writes, and with one in flight it waits for
+// every outstanding ds_read (lgkmcnt(0)) instead of the one it needs, which
+// serialises the fragment prefetch.  The asm has no outputs (it writes only
+// LDS), and its completion is tracked by this kernel's own vmcnt accounting
+// (wait_vmem); compiler-placed vmcnt waits only become stricter when these
+// extra loads are outstanding.  M0 is set inside the asm, with the one wait
+// state the hardware needs before the DMA reads it; nothing else in these
+// kernels keeps a value in M0.
+typedef int v4i_rsrc __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
 
-__device__ __forceinline__ void lds_dma4(const void* src, void* lds_dst) {
-  __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)lds_dst, 4, 0, 0);
+// Buffer descriptor of `bytes` bytes at `base` (wave-uniform values).
+__device__ __forceinline__ v4i_rsrc make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  v4i_rsrc r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;  // 32-bit data format; offsets past num_records read as zero
+  return r;
+}
+
+__device__ __forceinline__ void lds_dma16(v4i_rsrc rs, uint32_t voff, uint32_t soff, void* lds_dst) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rs), "s"(soff), "s"(lds_addr(lds_dst)) : "memory", "m0");
+}
+
+__device__ __forceinline__ void lds_dma4(v4i_rsrc rs, uint32_t voff, uint32_t soff, void* lds_dst) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rs), "s"(soff), "s"(lds_addr(lds_dst)) : "memory", "m0");
 }
 
 // Wait until at most N of this wave's vector-memory loads (LDS DMA included)
@@ -189,7 +225,12 @@ __device__ __forceinline__ int loads_ahead(int kb, int KB) {
 // LDS slot swizzle of tile row r (see the layout note at the top)
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
-template <int BM, int BN, int WM, int WN, int NST, int VAR>
+// SCHED selects the main-loop schedule: kInterleaved (every wave loads and
+// computes each slab; one barrier per slab) or kPingPong (8 waves in two
+// groups that alternate load and compute steps, see below).
+enum Schedule { kInterleaved = 0, kPingPong = 1 };
+
+template <int BM, int BN, int WM, int WN, int NST, int VAR, int SCHED = kInterleaved>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p) {
   constexpr int kThreads = WM * WN * 64;
   constexpr int kWaves = WM * WN;
@@ -277,32 +318,37 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   // ---- slab loader.  One wave-wide DMA instruction moves 1 KiB (one
   // fragment half) into LDS; each wave owns a fixed set of instructions whose
   // per-lane source offsets are computed once per tile.
-  constexpr int kPerWaveA = kJa / kWaves;
-  constexpr int kPerWaveB = kJb / kWaves;
-  static_assert(kJa % kWaves == 0 && kJb % kWaves == 0, "DMA instructions must split evenly over waves");
+  // Instruction j of a slab belongs to wave j % kWaves; when the count does
+  // not divide evenly (e.g. BN = 224) the first waves issue one more.
+  constexpr int kPerWaveA = (kJa + kWaves - 1) / kWaves;
+  constexpr int kPerWaveB = (kJb + kWaves - 1) / kWaves;
   uint32_t a_off[kPerWaveA];
   uint32_t b_off[kPerWaveB];
   int a_live = 0;  // A DMA instructions this wave issues per slab (masked skips empty fragments)
+  int b_live = 0;  // B DMA instructions this wave issues per slab
   // instruction j covers tile rows 8j..8j+7; lane l fills LDS slot (l & 7) of
   // row 8j + (l >> 3) with the global chunk that belongs there
-#pragma unroll
+  #pragma unroll
   for (int jj = 0; jj < kPerWaveA; ++jj) {
     const int j = jj * kWaves + wave;
     const int r = 8 * j + (lane >> 3);
     const int chunk = (lane & 7) ^ swz(r);
     int row = m0 + r;
     row = row < row_limit ? row : row_limit - 1;
-    a_off[jj] = (uint32_t)row * (uint32_t)K + 16u * chunk;
-    a_live += (m0 + 8 * j < a_rows) ? 1 : 0;
+    // row * K is a multiple of 128 and the chunk offset is below 128: OR keeps
+    // the offset one 32-bit value (an add lets the compiler form a 64-bit mad)
+    a_off[jj] = ((uint32_t)row * (uint32_t)K) | (16u * chunk);
+    a_live += (j < kJa && m0 + 8 * j < a_rows) ? 1 : 0;
   }
-#pragma unroll
+  #pragma unroll
   for (int jj = 0; jj < kPerWaveB; ++jj) {
     const int j = jj * kWaves + wave;
     const int r = 8 * j + (lane >> 3);
     const int chunk = (lane & 7) ^ swz(r);
     int row = n0 + r;
     row = row < p.n ? row : p.n - 1;
-    b_off[jj] = (uint32_t)row * (uint32_t)K + 16u * chunk;
+    b_off[jj] = ((uint32_t)row * (uint32_t)K) | (16u * chunk);
+    b_live += j < kJb ? 1 : 0;
   }
   // Row scales: BM floats, one dword instruction per 64 rows.  Every wave
   // issues exactly one (waves past the needed count repeat a block with the
@@ -325,37 +371,50 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
     blk = blk < p.nb_count ? blk : p.nb_count - 1;
     sb_off = (uint32_t)blk * (uint32_t)p.kb_count;  // sfb row stride: all K slabs
   }
-  const int c_loads = a_live + kPerWaveB + 2;
+  const int c_loads = a_live + b_live + 2;
 
-  auto issue_slab = [&](int kl, int buf) {
+  // Buffer descriptors of this tile's operands (sizes in bytes; the host
+  // keeps every operand below 4 GiB).
+  const v4i_rsrc rs_a = make_rsrc(A, (uint32_t)row_limit * (uint32_t)K);
+  const v4i_rsrc rs_b = make_rsrc(B, (uint32_t)p.n * (uint32_t)K);
+  const v4i_rsrc rs_sa = make_rsrc(SFA, (uint32_t)p.kb_count * (uint32_t)p.sfa_ld * 4u);
+  const v4i_rsrc rs_sb = make_rsrc(SFB, (uint32_t)p.nb_count * (uint32_t)p.kb_count * 4u);
+  // DMA instruction d (0 .. kNumDma-1) of this wave for slab kl into stage
+  // buf: the A rows, then the B rows, then the two scale loads.
+  constexpr int kNumDma = kPerWaveA + kPerWaveB + 2;
+  auto issue_one = [&](int kl, int buf, int d) {
     const int kb = kb0 + kl;  // global slab index
     uint8_t* st = smem + buf * S::kStage;
-    const uint8_t* a_k = A + kb * kSlab;
-    const uint8_t* b_k = B + kb * kSlab;
-#pragma unroll
-    for (int jj = 0; jj < kPerWaveA; ++jj) {
+    if (d < kPerWaveA) {
+      const int j = d * kWaves + wave;
+      if (kJa % kWaves != 0 && j >= kJa) return;
+      if (VAR == kMasked && m0 + 8 * j >= a_rows) return;  // rows without results
+      lds_dma16(rs_a, a_off[d], (uint32_t)kb * kSlab, st + j * kDmaBytes);
+    } else if (d < kPerWaveA + kPerWaveB) {
+      const int jj = d - kPerWaveA;
       const int j = jj * kWaves + wave;
-      if (VAR == kMasked && m0 + 8 * j >= a_rows) continue;  // rows without results
-      lds_dma16(a_k + a_off[jj], st + j * kDmaBytes);
+      if (kJb % kWaves != 0 && j >= kJb) return;
+      lds_dma16(rs_b, b_off[jj], (uint32_t)kb * kSlab, st + S::kA + j * kDmaBytes);
+    } else if (d == kPerWaveA + kPerWaveB) {
+      if (sa_lane) lds_dma4(rs_sa, sa_off * 4u, (uint32_t)kb * (uint32_t)p.sfa_ld * 4u, st + S::kA + S::kB + sa_blk * 256);
+    } else {
+      if (sb_lane) lds_dma4(rs_sb, sb_off * 4u, (uint32_t)kb * 4u, st + S::kA + S::kB + S::kSa);
     }
-#pragma unroll
-    for (int jj = 0; jj < kPerWaveB; ++jj) {
-      const int j = jj * kWaves + wave;
-      lds_dma16(b_k + b_off[jj], st + S::kA + j * kDmaBytes);
-    }
-    if (sa_lane) lds_dma4(SFA + (size_t)kb * p.sfa_ld + sa_off, st + S::kA + S::kB + sa_blk * 256);
-    if (sb_lane) lds_dma4(SFB + sb_off + kb, st + S::kA + S::kB + S::kSa);
+  };
+  auto issue_slab = [&](int kl, int buf) {
+    #pragma unroll
+    for (int d = 0; d < kNumDma; ++d) issue_one(kl, buf, d);
   };
 
   v4f acc[FM][FN];
-#pragma unroll
+  #pragma unroll
   for (int i = 0; i < FM; ++i)
-#pragma unroll
+    #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // index of each fragment's B scale block among the tile's blocks
   int sb_idx[FN];
-#pragma unroll
+  #pragma unroll
   for (int j = 0; j < FN; ++j) sb_idx[j] = ((n0 + wn * TN + j * 16) >> 7) - nb0;
   constexpr bool kSbUniform = (128 % TN) == 0;  // a wave's columns lie in one block
   // fragments of this wave that hold at least one valid row
@@ -371,81 +430,235 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   const uint32_t frag_lo = (uint32_t)(fr * 128 + 16 * ((lane >> 4) ^ swz(fr)));
   const uint32_t frag_hi = (uint32_t)(fr * 128 + 16 * ((4 + (lane >> 4)) ^ swz(fr)));
 
-  // ---- prologue: DMA of slabs 0..NST-2
-#pragma unroll
-  for (int s0 = 0; s0 <= NST - 2; ++s0)
-    if (s0 < KB) issue_slab(s0, s0);
-
-  for (int kb = 0; kb < KB; ++kb) {
-    // slab kb's DMA must have landed (in every wave: then the barrier); the
-    // loads issued after it may stay in flight.
-    wait_vmem_dyn(c_loads * loads_ahead<NST>(kb, KB));
-    block_barrier();  // also: every wave is done with the stage about to be refilled
-    __builtin_amdgcn_sched_barrier(0);
-    if (kb + NST - 1 < KB) issue_slab(kb + NST - 1, (kb + NST - 1) % NST);
-    __builtin_amdgcn_sched_barrier(0);
-
-    const uint8_t* st = smem + (kb % NST) * S::kStage;
-    const uint8_t* sA = st;
-    const uint8_t* sB = st + S::kA;
-    const float* sSa = (const float*)(st + S::kA + S::kB);
-    const float* sSb = (const float*)(st + S::kA + S::kB + S::kSa);
-
-    float sbv[FN];
-#pragma unroll
-    for (int j = 0; j < FN; ++j) sbv[j] = sSb[kSbUniform ? sb_idx[0] : sb_idx[j]];
-
-    v8i bf[FN];
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int f = wn * FN + j;
-      const v4i lo = *(const v4i*)(sB + f * 2048 + frag_lo);
-      const v4i hi = *(const v4i*)(sB + f * 2048 + frag_hi);
-      bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
-
-    // Software pipeline over the wave's FM x FN fragments (row-major order t):
-    // A rows are read from LDS kPf rows ahead, and fragment t's promotion
-    // runs kLag fragments after its MFMA, so each MFMA has independent
-    // promotion FMAs of earlier fragments to co-issue with.
-    constexpr int kPf = FM < 2 ? FM : 2;
-    constexpr int kAbuf = kPf + 1;
-    constexpr int kSabuf = kPf + 2;
-    constexpr int kLag = 2;
-    constexpr int F = FM * FN;
-    v8i abuf[kAbuf];
-    v4f sabuf[kSabuf];
-    v4f pr[kLag + 1];
-    auto load_a = [&](int i) {
-      const int f = wm * FM + i;
-      const v4i lo = *(const v4i*)(sA + f * 2048 + frag_lo);
-      const v4i hi = *(const v4i*)(sA + f * 2048 + frag_hi);
-      abuf[i % kAbuf] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      sabuf[i % kSabuf] = *(const v4f*)(sSa + wm * TM + i * 16 + 4 * (lane >> 4));
+  if constexpr (SCHED == kPingPong) {
+    // ---- ping-pong schedule (256 x 256 tile, 8 waves, 2 stages).  Waves
+    // 0-3 (group 0, tile rows 0-127) and waves 4-7 (group 1, rows 128-255)
+    // sit two per SIMD, one of each group.  Each wave cuts its slab work
+    // into kNch chunks of kFh A fragments and alternates a load step (LDS ->
+    // registers: the slab's B fragments with chunk 0, then the chunk's A
+    // fragments and row scales) and a compute step (the chunk's MFMAs and
+    // promotions), with a workgroup barrier after every step.  Group 1 runs
+    // one step behind group 0, so on every SIMD one wave feeds the matrix
+    // core while the other moves data: LDS reads and LDS DMA overlap MFMA
+    // work instead of alternating with it.  Steps of slab kb (2 * kNch):
+    //
+    //   step 2c     group 0: load (kb, c)        group 1: compute the chunk before (kb, c)
+    //   step 2c+1   group 0: compute (kb, c)     group 1: load (kb, c)
+    //
+    // with the DMA of slab kb+1 issued in each group's first load step of
+    // slab kb.  Slab kb is read only in its own 2 * kNch steps; slab kb+1
+    // goes to the other stage, last read in the step before, and every wave
+    // waits for its own DMA before the barrier that closes slab kb.  Every
+    // step ends with lgkmcnt(0), so no LDS read is in flight when a stage is
+    // refilled.
+    static_assert(BM == 256 && BN == 256 && WM == 2 && WN == 4 && NST == 2, "ping-pong tile shape");
+    static_assert(kSbUniform, "a wave's columns must share one B scale block");
+    constexpr int kFh = 4;          // A fragments per chunk
+    constexpr int kNch = FM / kFh;  // chunks per slab
+    const int grp = wm;
+    // The per-fragment validity test is a run-time branch for every variant
+    // (dense: always true).  The uniform branches cost a scalar compare each,
+    // and they keep the scheduler from hoisting the next steps' loads, which
+    // otherwise raises register pressure past the 256-VGPR budget.
+    asm volatile("" : "+s"(fm_valid));
+    v8i bq[FN];
+    v8i aq[kFh];
+    v4f sq[kFh];
+    float sbq = 0.f;
+    // LDS reads address a per-step base register plus an immediate offset;
+    // the opaque base keeps the compiler from precomputing a register per
+    // fragment and stage (a stage is wider than the 16-bit offset field).
+    auto lds_base = [&](const void* p0) {
+      uint32_t b = lds_addr(p0);
+      asm volatile("" : "+v"(b));
+      return b;
     };
+    auto rd16 = [&](uint32_t addr) { return *(const __attribute__((address_space(3))) v4i*)(uintptr_t)addr; };
+    auto load_chunk = [&](int kb, int c) {
+      const uint8_t* st = smem + (kb & 1) * S::kStage;
+      if (c == 0) {
+        const float* sSb = (const float*)(st + S::kA + S::kB + S::kSa);
+        sbq = sSb[sb_idx[0]];
+        const uint32_t bb_lo = lds_base(st + S::kA + wn * FN * 2048) + frag_lo;
+        const uint32_t bb_hi = bb_lo - frag_lo + frag_hi;
 #pragma unroll
-    for (int i = 0; i < kPf; ++i)
-      if (VAR != kMasked || i < fm_valid) load_a(i);
-#pragma unroll
-    for (int t = 0; t < F + kLag; ++t) {
-      if (t < F) {
-        const int i = t / FN, j = t % FN;
-        if (VAR != kMasked || i < fm_valid) {
-          if (j == 0 && i + kPf < FM && (VAR != kMasked || i + kPf < fm_valid)) load_a(i + kPf);
-          pr[t % (kLag + 1)] = mfma_fp8_16x16x128(abuf[i % kAbuf], bf[j]);
+        for (int j = 0; j < FN; ++j) {
+          const v4i lo = rd16(bb_lo + j * 2048);
+          const v4i hi = rd16(bb_hi + j * 2048);
+          bq[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
       }
-      if (t >= kLag) {
-        const int u = t - kLag;
-        const int i = u / FN, j = u % FN;
-        if (VAR != kMasked || i < fm_valid) {
-          const v4f sc = sabuf[i % kSabuf] * sbv[j];
-          const v4f pv = pr[u % (kLag + 1)];
-          acc[i][j][0] = __builtin_fmaf(pv[0], sc[0], acc[i][j][0]);
-          acc[i][j][1] = __builtin_fmaf(pv[1], sc[1], acc[i][j][1]);
-          acc[i][j][2] = __builtin_fmaf(pv[2], sc[2], acc[i][j][2]);
-          acc[i][j][3] = __builtin_fmaf(pv[3], sc[3], acc[i][j][3]);
+      const uint32_t ab_lo = lds_base(st + (wm * FM + c * kFh) * 2048) + frag_lo;
+      const uint32_t ab_hi = ab_lo - frag_lo + frag_hi;
+      const uint32_t sab = lds_base(st + S::kA + S::kB + (wm * TM + c * kFh * 16) * 4) + 16 * (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < kFh; ++i) {
+        if (c * kFh + i >= fm_valid) continue;
+        const v4i lo = rd16(ab_lo + i * 2048);
+        const v4i hi = rd16(ab_hi + i * 2048);
+        aq[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const v4i sv = rd16(sab + i * 64);
+        sq[i] = v4f{__int_as_float(sv[0]), __int_as_float(sv[1]), __int_as_float(sv[2]), __int_as_float(sv[3])};
+      }
+    };
+    // MFMA of fragment t, promotion of fragment t - 2 (its result is ready
+    // by then); the fixed order keeps promotions away from their MFMA.
+    auto compute_chunk = [&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      constexpr int kLagPP = 2;
+      v4f pr[kLagPP + 1];
+#pragma unroll
+      for (int t = 0; t < kFh * FN + kLagPP; ++t) {
+        if (t < kFh * FN) {
+          const int i = t / FN, j = t % FN;
+          if (c * kFh + i < fm_valid) pr[t % (kLagPP + 1)] = mfma_fp8_16x16x128(aq[i], bq[j]);
         }
+        if (t >= kLagPP) {
+          const int u = t - kLagPP;
+          const int i = u / FN, j = u % FN;
+          if (c * kFh + i < fm_valid) {
+            const v4f sc = sq[i] * sbq;
+            const v4f pv = pr[u % (kLagPP + 1)];
+            acc[c * kFh + i][j][0] = __builtin_fmaf(pv[0], sc[0], acc[c * kFh + i][j][0]);
+            acc[c * kFh + i][j][1] = __builtin_fmaf(pv[1], sc[1], acc[c * kFh + i][j][1]);
+            acc[c * kFh + i][j][2] = __builtin_fmaf(pv[2], sc[2], acc[c * kFh + i][j][2]);
+            acc[c * kFh + i][j][3] = __builtin_fmaf(pv[3], sc[3], acc[c * kFh + i][j][3]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    auto end_step = [&]() {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
+      block_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // static loop over the chunks of a slab (c is a compile-time constant)
+    auto for_chunks = [&](auto body) {
+      [&]<int... C>(std::integer_sequence<int, C...>) {
+        (body(std::integral_constant<int, C>{}), ...);
+      }(std::make_integer_sequence<int, kNch>{});
+    };
+
+    if (KB > 0) issue_slab(0, 0);
+    wait_vmem_all();
+    block_barrier();
+    // The two groups run separate copies of the loop (the same number of
+    // barriers each): with one loop and per-step branches on the group, the
+    // compiler cannot tell the paths apart and keeps extra live copies of
+    // the fragment registers.
+    if (grp == 0) {
+      for (int kb = 0; kb < KB; ++kb) {
+        for_chunks([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          load_chunk(kb, c);
+          if (c == 0 && kb + 1 < KB) issue_slab(kb + 1, (kb + 1) & 1);
+          end_step();
+          compute_chunk(cc);
+          if (c == kNch - 1) wait_vmem_all();  // this wave's share of slab kb+1 has landed
+          end_step();
+        });
+      }
+      end_step();  // group 1 finishes its last chunk
+    } else {
+      for (int kb = 0; kb < KB; ++kb) {
+        for_chunks([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          if (c == 0) {
+            if (kb > 0) compute_chunk(std::integral_constant<int, kNch - 1>{});
+          } else {
+            compute_chunk(std::integral_constant<int, (c > 0 ? c - 1 : 0)>{});
+          }
+          end_step();
+          load_chunk(kb, c);
+          if (c == 0 && kb + 1 < KB) issue_slab(kb + 1, (kb + 1) & 1);
+          if (c == kNch - 1) wait_vmem_all();
+          end_step();
+        });
+      }
+      if (KB > 0) compute_chunk(std::integral_constant<int, kNch - 1>{});
+      end_step();
+    }
+  } else {
+    // ---- prologue: DMA of slabs 0..NST-2
+    #pragma unroll
+    for (int s0 = 0; s0 <= NST - 2; ++s0)
+      if (s0 < KB) issue_slab(s0, s0);
+
+    for (int kb = 0; kb < KB; ++kb) {
+      // slab kb's DMA must have landed (in every wave: then the barrier); the
+      // loads issued after it may stay in flight.
+      wait_vmem_dyn(c_loads * loads_ahead<NST>(kb, KB));
+      block_barrier();  // also: every wave is done with the stage about to be refilled
+      __builtin_amdgcn_sched_barrier(0);
+      if (kb + NST - 1 < KB) issue_slab(kb + NST - 1, (kb + NST - 1) % NST);
+      __builtin_amdgcn_sched_barrier(0);
+
+      const uint8_t* st = smem + (kb % NST) * S::kStage;
+      const uint8_t* sA = st;
+      const uint8_t* sB = st + S::kA;
+      const float* sSa = (const float*)(st + S::kA + S::kB);
+      const float* sSb = (const float*)(st + S::kA + S::kB + S::kSa);
+
+      float sbv[FN];
+      #pragma unroll
+      for (int j = 0; j < FN; ++j) sbv[j] = sSb[kSbUniform ? sb_idx[0] : sb_idx[j]];
+
+      v8i bf[FN];
+      #pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int f = wn * FN + j;
+        const v4i lo = *(const v4i*)(sB + f * 2048 + frag_lo);
+        const v4i hi = *(const v4i*)(sB + f * 2048 + frag_hi);
+        bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+
+      // Software pipeline over the wave's FM x FN fragments (row-major order t):
+      // A rows are read from LDS kPf rows ahead, and fragment t's promotion
+      // runs kLag fragments after its MFMA, so each MFMA has independent
+      // promotion FMAs of earlier fragments to co-issue with.
+      constexpr int kPf = FM < 2 ? FM : 2;
+      constexpr int kAbuf = kPf + 1;
+      constexpr int kSabuf = kPf + 2;
+      constexpr int kLag = 2;
+      constexpr int F = FM * FN;
+      v8i abuf[kAbuf];
+      v4f sabuf[kSabuf];
+      v4f pr[kLag + 1];
+      auto load_a = [&](int i) {
+        const int f = wm * FM + i;
+        const v4i lo = *(const v4i*)(sA + f * 2048 + frag_lo);
+        const v4i hi = *(const v4i*)(sA + f * 2048 + frag_hi);
+        abuf[i % kAbuf] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        sabuf[i % kSabuf] = *(const v4f*)(sSa + wm * TM + i * 16 + 4 * (lane >> 4));
+      };
+      #pragma unroll
+      for (int i = 0; i < kPf; ++i)
+        if (VAR != kMasked || i < fm_valid) load_a(i);
+      #pragma unroll
+      for (int t = 0; t < F + kLag; ++t) {
+        if (t < F) {
+          const int i = t / FN, j = t % FN;
+          if (VAR != kMasked || i < fm_valid) {
+            if (j == 0 && i + kPf < FM && (VAR != kMasked || i + kPf < fm_valid)) load_a(i + kPf);
+            pr[t % (kLag + 1)] = mfma_fp8_16x16x128(abuf[i % kAbuf], bf[j]);
+          }
+        }
+        if (t >= kLag) {
+          const int u = t - kLag;
+          const int i = u / FN, j = u % FN;
+          if (VAR != kMasked || i < fm_valid) {
+            const v4f sc = sabuf[i % kSabuf] * sbv[j];
+            const v4f pv = pr[u % (kLag + 1)];
+            acc[i][j][0] = __builtin_fmaf(pv[0], sc[0], acc[i][j][0]);
+            acc[i][j][1] = __builtin_fmaf(pv[1], sc[1], acc[i][j][1]);
+            acc[i][j][2] = __builtin_fmaf(pv[2], sc[2], acc[i][j][2]);
+            acc[i][j][3] = __builtin_fmaf(pv[3], sc[3], acc[i][j][3]);
+          }
+        }
+        // keep this order: a promotion must not move up next to the MFMA
+        // that produces its input (that stalls the wave on the result)
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -459,15 +672,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   // which are coherent across the per-XCD L2s (the agent-scope path), so no
   // L2 write-back or invalidate is needed.  The reducer reads kChunk splits'
   // partials per batch; loads past the last split return zero.
-  if (VAR == kDense && p.splits > 1) {
+  if constexpr (VAR == kDense && SCHED == kInterleaved) if (p.splits > 1) {
     constexpr int kTileFloats = BM * BN;
     constexpr int kChunk = (FM * FN * 4) >= 128 ? 1 : 128 / (FM * FN * 4);
     float* part = p.ws_partial + (size_t)tile_id * p.splits * kTileFloats;
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(part, 0, p.splits * kTileFloats * 4, kBufferRsrcWord3);
-#pragma unroll
+    #pragma unroll
     for (int i = 0; i < FM; ++i)
-#pragma unroll
+      #pragma unroll
       for (int j = 0; j < FN; ++j)
         __builtin_amdgcn_raw_buffer_store_b128(
             acc[i][j], rs, (split * kTileFloats + (((wave * FM + i) * FN + j) * 64 + lane) * 4) * 4, 0, kCpolSc1);
@@ -479,25 +692,25 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
     }
     __syncthreads();
     if (s_flag == 0) return;  // not the last split: done
-#pragma unroll
+    #pragma unroll
     for (int i = 0; i < FM; ++i)
-#pragma unroll
+      #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
     for (int sp0 = 0; sp0 < p.splits; sp0 += kChunk) {
       v4f part_v[kChunk][FM][FN];
-#pragma unroll
+      #pragma unroll
       for (int c = 0; c < kChunk; ++c)
-#pragma unroll
+        #pragma unroll
         for (int i = 0; i < FM; ++i)
-#pragma unroll
+          #pragma unroll
           for (int j = 0; j < FN; ++j)
             part_v[c][i][j] = __builtin_amdgcn_raw_buffer_load_b128(
                 rs, ((sp0 + c) * kTileFloats + (((wave * FM + i) * FN + j) * 64 + lane) * 4) * 4, 0, kCpolSc1);
-#pragma unroll
+      #pragma unroll
       for (int c = 0; c < kChunk; ++c)
-#pragma unroll
+        #pragma unroll
         for (int i = 0; i < FM; ++i)
-#pragma unroll
+          #pragma unroll
           for (int j = 0; j < FN; ++j) acc[i][j] += part_v[c][i][j];
     }
     if (threadIdx.x == 0)  // ready for the next call
@@ -508,13 +721,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   // coalesced row stores of valid rows and columns
   block_barrier();  // every wave is done reading the last stage
   uint8_t* so = smem;
-#pragma unroll
+  #pragma unroll
   for (int i = 0; i < FM; ++i) {
     if (VAR == kMasked && i >= fm_valid) continue;
-#pragma unroll
+    #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int cl = wn * TN + j * 16 + (lane & 15);
-#pragma unroll
+      #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int rl = wm * TM + i * 16 + 4 * (lane >> 4) + e;
         *(uint16_t*)(so + rl * S::kOutPitch + cl * 2) = f32_to_bf16_rne(acc[i][j][e]);

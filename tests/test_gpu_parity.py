@@ -21,7 +21,8 @@ from tests import gpu_harness as H
 pytestmark = pytest.mark.gpu
 
 DENSE_CONFIGS = ["dense_256x256_w8_s2", "dense_256x128_w8_s3", "dense_128x256_w8_s3", "dense_128x128_w4_s3",
-                 "dense_128x128_w4_s2", "dense_64x64_w4_s3", "dense_64x64_w4_s8", "dense_64x32_w4_s4", "dense_256x128_w4_s2",
+                 "dense_128x128_w4_s2", "dense_64x64_w4_s3", "dense_64x64_w4_s8", "dense_64x32_w4_s4", "dense_256x224_w8_s2",
+                 "dense_128x256_w4_s3_wide", "dense_256x256_w8_s2_pp", "dense_256x128_w4_s2",
                  "dense_256x128_w4_s3", "dense_128x256_w4_s3"]
 
 
@@ -82,7 +83,7 @@ def test_dense_unit_scale_exact_values(gpu):
 
 
 @pytest.mark.parametrize("cfg", [None, "contig_128x256_w8_s3", "contig_128x128_w4_s3", "contig_128x128_w4_s2",
-                                 "contig_128x256_w8_s2"])
+                                 "contig_128x256_w8_s2", "contig_128x256_w4_s3", "contig_128x256_w4_s2"])
 def test_contiguous(gpu, cfg, monkeypatch):
     if cfg:
         monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
@@ -107,7 +108,9 @@ def test_contiguous(gpu, cfg, monkeypatch):
 
 @pytest.mark.parametrize("cfg,max_m", [(None, 96), (None, 256), ("masked_256x128_w4_s2", 300),
                                        ("masked_256x128_w4_s3", 200), ("masked_64x64_w4_s3", 130),
-                                       ("masked_256x256_w8_s2", 300)])
+                                       ("masked_256x256_w8_s2", 300), ("masked_256x256_w8_s2_pp", 300),
+                                       ("masked_256x256_w8_s2_pp", 200), ("masked_256x128_w8_s2", 300),
+                                       ("masked_256x128_w8_s2", 100)])
 def test_masked(gpu, cfg, max_m, monkeypatch):
     if cfg:
         monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
