@@ -25,7 +25,7 @@ Modules
 -------
 e4m3   exact 256-entry decode table, round-to-nearest-even saturating encoder
 quant  1x128 (activation) and 128x128 (weight) quantisers
-gemm   dense, contiguous-grouped and masked-grouped reference GEMMs in fp64
+gemm   dense, contiguous-grouped, masked-grouped and K-grouped reference GEMMs in fp64
 check  the element-wise acceptance rule
 """
 
@@ -36,5 +36,7 @@ from .gemm import (  # noqa: F401
     gemm_nt_ref_at,
     grouped_contiguous_ref,
     grouped_masked_ref,
+    k_grouped_ref,
+    k_grouped_ref_at,
 )
 from .check import tolerance_check, bf16_bits_to_float, bf16_round  # noqa: F401

@@ -30,6 +30,16 @@ The grouped layouts follow the same page (MoE items):
   (clamped to [0, max_m]); rows at or past that count have no result.
 
 Invalid entries are returned as NaN together with a boolean validity mask.
+
+The K-grouped layout is named on "DeepGEMM: making LLM matrix
+multiplication fly" (pomoai.com), "core functions", next to the M-grouped
+one, for the irregular shapes of MoE training; the pages give no more than
+the name.  The reading taken here: G groups are concatenated along K, group g
+owning the k_sizes[g] consecutive K columns that follow the groups before it
+(each size a multiple of 128, so every group is a run of whole scale slabs),
+and D[g] = A[:, K_g] . B[:, K_g]^T with the same 1x128 / 128x128 scales as
+the dense GEMM (the weight-gradient use: tokens on K).  An empty group's
+result is the empty sum, zero.
 """
 
 import numpy as np
@@ -174,4 +184,54 @@ def grouped_masked_ref_at(qa, sfa, qb, sfb, masked_m, groups, rows, cols):
         sa = np.asarray(sfa, np.float64)
         sb = np.asarray(sfb, np.float64)
         out[ok] = _entries(qa[gg, rr], sa[gg, rr], qb[gg, cc], sb[gg, cc // SLAB])
+    return out
+
+
+def _k_ranges(k_sizes, k_total):
+    """Slab ranges [s0, s1) of the K groups; raises on sizes that are negative,
+    not whole slabs, or past k_total."""
+    sizes = np.asarray(k_sizes, np.int64)
+    if np.any(sizes < 0) or np.any(sizes % SLAB):
+        raise ValueError("k_sizes must be non-negative multiples of 128")
+    ends = np.cumsum(sizes)
+    if ends.size and ends[-1] > k_total:
+        raise ValueError("k_sizes add up to more than K")
+    starts = ends - sizes
+    return [(int(a) // SLAB, int(b) // SLAB) for a, b in zip(starts, ends)]
+
+
+def k_grouped_ref(qa, sfa, qb, sfb, k_sizes):
+    """K-grouped reference.  qa: M x K, sfa: M x K/128, qb: N x K,
+    sfb: ceil(N/128) x K/128, k_sizes: G group sizes along K.  Returns the
+    G x M x N fp64 results, group g computed on its own K columns only."""
+    qa = np.asarray(qa, np.uint8)
+    qb = np.asarray(qb, np.uint8)
+    m, n, k, _ = _shapes(qa, sfa, qb, sfb)
+    ranges = _k_ranges(k_sizes, k)
+    r = np.zeros((len(ranges), m, n), dtype=np.float64)
+    for g, (s0, s1) in enumerate(ranges):
+        if s1 > s0:
+            cols = slice(s0 * SLAB, s1 * SLAB)
+            r[g] = gemm_nt_ref(qa[:, cols], np.asarray(sfa)[:, s0:s1], qb[:, cols], np.asarray(sfb)[:, s0:s1])
+    return r
+
+
+def k_grouped_ref_at(qa, sfa, qb, sfb, k_sizes, groups, rows, cols):
+    """K-grouped reference at (groups[i], rows[i], cols[i])."""
+    qa = np.asarray(qa, np.uint8)
+    qb = np.asarray(qb, np.uint8)
+    ranges = _k_ranges(k_sizes, qa.shape[1])
+    groups = np.asarray(groups, np.int64)
+    rows = np.asarray(rows, np.int64)
+    cols = np.asarray(cols, np.int64)
+    sa = np.asarray(sfa, np.float64)
+    sb = np.asarray(sfb, np.float64)
+    out = np.zeros(rows.shape, dtype=np.float64)
+    for g in np.unique(groups):
+        s0, s1 = ranges[g]
+        sel = np.nonzero(groups == g)[0]
+        if s1 > s0:
+            kc = slice(s0 * SLAB, s1 * SLAB)
+            rr, cc = rows[sel], cols[sel]
+            out[sel] = _entries(qa[rr, kc], sa[rr, s0:s1], qb[cc, kc], sb[cc // SLAB, s0:s1])
     return out

@@ -8,7 +8,10 @@
 * invariants: scaling a row of sa scales that row of the result exactly,
   the _at variants agree with the full ones bit for bit;
 * grouped layouts against the brute force: each row uses its own expert's B,
-  padding rows and rows past masked_m have no result, masked_m is clamped.
+  padding rows and rows past masked_m have no result, masked_m is clamped;
+* the K-grouped layout against the brute force on each group's K columns,
+  its groups summing to the dense result, unit scales giving a plain matmul
+  per K slice, an empty group giving zero, and bad group sizes rejected.
 """
 
 from fractions import Fraction
@@ -18,7 +21,7 @@ import pytest
 import torch
 
 from oracle import (gemm_nt_ref, gemm_nt_ref_at, grouped_contiguous_ref,
-                    grouped_masked_ref, tolerance_check)
+                    grouped_masked_ref, k_grouped_ref, k_grouped_ref_at, tolerance_check)
 from oracle.gemm import grouped_contiguous_ref_at, grouped_masked_ref_at
 
 SPECIAL = np.array([0x7E, 0xFE, 0x01, 0x81, 0x00, 0x80, 0x07, 0x08, 0x38, 0x5F], dtype=np.uint8)
@@ -226,3 +229,63 @@ def test_tolerance_rule():
     d[2] = np.nan
     res = tolerance_check(d, r)
     assert not res["ok"] and res["n_bad"] == 1
+
+
+# ---- K-grouped layout (groups concatenated along K)
+
+def test_k_grouped_against_brute_force():
+    # three groups of 1, 0 and 2 slabs over K = 512 (the last slab unused)
+    rng = np.random.default_rng(21)
+    m, n, k = 3, 4, 512
+    qa, qb = random_codes(rng, (m, k)), random_codes(rng, (n, k))
+    sa, sb = random_scales(rng, (m, 4)), random_scales(rng, (1, 4))
+    sizes = [128, 0, 256]
+    got = k_grouped_ref(qa, sa, qb, sb, sizes)
+    assert got.shape == (3, m, n)
+    assert np.all(got[1] == 0.0)  # an empty group is the empty sum
+    exact0, mag0 = brute(qa[:, 0:128], sa[:, 0:1], qb[:, 0:128], sb[:, 0:1])
+    assert_close_to_exact(got[0], exact0, mag0, 1)
+    exact2, mag2 = brute(qa[:, 128:384], sa[:, 1:3], qb[:, 128:384], sb[:, 1:3])
+    assert_close_to_exact(got[2], exact2, mag2, 2)
+
+
+def test_k_grouped_sums_to_dense():
+    # linearity: the groups' results add up to the dense result over the
+    # K columns they cover (up to fp64 rounding of the regrouped sum)
+    rng = np.random.default_rng(22)
+    m, n, k = 9, 140, 1280
+    qa, qb = random_codes(rng, (m, k)), random_codes(rng, (n, k))
+    sa, sb = random_scales(rng, (m, 10)), random_scales(rng, (2, 10))
+    sizes = [384, 128, 0, 512]  # 8 of the 10 slabs
+    got = k_grouped_ref(qa, sa, qb, sb, sizes).sum(axis=0)
+    dense = gemm_nt_ref(qa[:, :1024], sa[:, :8], qb[:, :1024], sb[:, :8])
+    da, db = lib_decode(qa[:, :1024]), lib_decode(qb[:, :1024])
+    scale_mag = np.abs(da) @ np.abs(db).T * sa[:, :8].max() * sb[:, :8].max()
+    assert np.all(np.abs(got - dense) <= 1e-14 * scale_mag + 0.0)
+
+
+def test_k_grouped_unit_scales_equal_plain_matmul():
+    rng = np.random.default_rng(23)
+    m, n, k = 17, 33, 768
+    qa, qb = random_codes(rng, (m, k)), random_codes(rng, (n, k))
+    sizes = [256, 512]
+    got = k_grouped_ref(qa, np.ones((m, 6), np.float32), qb, np.ones((1, 6), np.float32), sizes)
+    da, db = torch.from_numpy(lib_decode(qa)), torch.from_numpy(lib_decode(qb))
+    assert np.array_equal(got[0], (da[:, :256] @ db[:, :256].T).numpy())
+    assert np.array_equal(got[1], (da[:, 256:] @ db[:, 256:].T).numpy())
+
+
+def test_k_grouped_at_matches_full_and_rejects_bad_sizes():
+    rng = np.random.default_rng(24)
+    m, n, k = 6, 130, 640
+    qa, qb = random_codes(rng, (m, k)), random_codes(rng, (n, k))
+    sa, sb = random_scales(rng, (m, 5)), random_scales(rng, (2, 5))
+    sizes = [128, 384, 0]
+    full = k_grouped_ref(qa, sa, qb, sb, sizes)
+    g = rng.integers(0, 3, 40)
+    r = rng.integers(0, m, 40)
+    c = rng.integers(0, n, 40)
+    assert np.array_equal(k_grouped_ref_at(qa, sa, qb, sb, sizes, g, r, c), full[g, r, c])
+    for bad in ([100], [-128], [512, 256]):
+        with pytest.raises(ValueError):
+            k_grouped_ref(qa, sa, qb, sb, bad)

@@ -36,6 +36,11 @@ MUTATIONS = [
      "out[ok] = _entries(qa[gg, rr], sa[gg, rr], qb[0, cc]"),
     ("gemm.py", "r[g, :c] = gemm_nt_ref(qa[g, :c], sfa[g, :c], qb[g], sfb[g])",
      "r[g, :c] = gemm_nt_ref(qa[g, :c], sfa[g, :c], qb[g], sfb[0])"),
+    # K-grouped: group start off by one slab, scales of the wrong slabs,
+    # unaligned sizes accepted
+    ("gemm.py", "starts = ends - sizes", "starts = ends - sizes + SLAB * (sizes > 0)"),
+    ("gemm.py", "np.asarray(sfa)[:, s0:s1], qb[:, cols]", "np.asarray(sfa)[:, 0:s1 - s0], qb[:, cols]"),
+    ("gemm.py", "if np.any(sizes < 0) or np.any(sizes % SLAB):", "if np.any(sizes < 0):"),
     # e4m3: tie rule, exponent bias, saturation code, subnormal boundary
     ("e4m3.py", "q = np.rint(steps)", "q = np.floor(steps + 0.5)"),
     ("e4m3.py", "mag = (8 + f) * 2.0 ** (e - 10)", "mag = (8 + f) * 2.0 ** (e - 9)"),
