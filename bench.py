@@ -163,6 +163,27 @@ def setup_workload(torch, np, dg, W, name, dev):
             dg.m_grouped_fp8_gemm_nt_contiguous((st["qa"], st["sfa"]), (st["qb"], st["sfb"]), st["d"], st["idx"])
 
         return w.kind, dict(m_indices=inp["m_indices"], g=len(s["group_rows"]), n=n, k=k), rot, launch, None, inp
+    if w.kind == "kgrouped":
+        m, n = s["m"], s["n"]
+        ks = torch.from_numpy(inp["k_sizes"]).to(dev)
+        k = inp["a"].shape[1]
+        qa, sfa = dg.quantize_a_1x128(torch.from_numpy(inp["a"]).to(dev))
+        qb, sfb = dg.quantize_b_128x128(torch.from_numpy(inp["b"]).to(dev))
+        g = ks.numel()
+
+        def make(i):
+            d = torch.empty((g, m, n), dtype=torch.bfloat16, device=dev)
+            if i == 0:
+                return {"qa": qa, "sfa": sfa, "qb": qb, "sfb": sfb, "d": d, "ks": ks}
+            return {"qa": qa.clone(), "sfa": sfa.clone(), "qb": qb.clone(), "sfb": sfb.clone(), "d": d,
+                    "ks": ks.clone()}
+
+        rot = Rotation(make, qa.numel() + qb.numel() + 2 * g * m * n)
+
+        def launch(st):
+            dg.k_grouped_fp8_gemm_nt((st["qa"], st["sfa"]), (st["qb"], st["sfb"]), st["d"], st["ks"])
+
+        return w.kind, dict(k_sizes=inp["k_sizes"], m=m, n=n, k=k), rot, launch, None, inp
     g, max_m, n, k = s["g"], s["max_m"], s["n"], s["k"]
     mm = torch.from_numpy(inp["masked_m"]).to(dev)
     qa, sfa = dg.quantize_a_1x128(torch.from_numpy(inp["a"]).to(dev))

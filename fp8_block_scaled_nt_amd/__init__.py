@@ -25,7 +25,8 @@ LIB_PATH = os.path.join(_PKG_DIR, "libdg.so")
 __all__ = [
     "DGError", "lib", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous",
     "m_grouped_fp8_gemm_nt_masked", "quantize_a_1x128", "quantize_b_128x128",
-    "get_m_alignment_for_contiguous_layout", "get_sfa_ld", "empty_sfa", "profile_next_launch",
+    "k_grouped_fp8_gemm_nt", "get_m_alignment_for_contiguous_layout", "get_sfa_ld", "empty_sfa",
+    "profile_next_launch",
     "reserve_workspace",
 ]
 
@@ -44,6 +45,7 @@ _SIGNATURES = {
     "dg_fp8_gemm_nt": [_vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _vp],
     "dg_m_grouped_fp8_gemm_nt_contiguous": [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _vp],
     "dg_m_grouped_fp8_gemm_nt_masked": [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _vp],
+    "dg_k_grouped_fp8_gemm_nt": [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _vp],
     "dg_get_m_alignment_for_contiguous_layout": [],
     "dg_get_sfa_ld": [_ci],
     "dg_quantize_a_1x128": [_vp, _vp, _vp, _ci, _ci, _vp],
@@ -193,6 +195,29 @@ def m_grouped_fp8_gemm_nt_masked(a_pair, b_pair, d, masked_m, expected_m=0):
     _check(lib().dg_m_grouped_fp8_gemm_nt_masked(
         _ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(d), _ptr(masked_m), g, max_m, n, k,
         int(expected_m), _stream()))
+    return d
+
+
+def k_grouped_fp8_gemm_nt(a_pair, b_pair, d, k_sizes):
+    """K-grouped GEMM: group g uses the k_sizes[g] K columns after the groups
+    before it; d: bf16 [g, m, n], written in place (zero for empty groups)."""
+    a, sfa = a_pair
+    b, sfb = b_pair
+    _need(a, "a", _FP8, 2)
+    _need(b, "b", _FP8, 2)
+    _need(d, "d", (torch.bfloat16,), 3)
+    _need(sfa, "sfa", (torch.float32,), 2)
+    _need(sfb, "sfb", (torch.float32,), 2)
+    _need(k_sizes, "k_sizes", (torch.int32,), 1)
+    m, k = a.shape
+    n = b.shape[0]
+    g = k_sizes.numel()
+    if b.shape[1] != k or tuple(d.shape) != (g, m, n):
+        raise ValueError(f"shape mismatch a{tuple(a.shape)} b{tuple(b.shape)} d{tuple(d.shape)} groups={g}")
+    if tuple(sfa.shape) != (k // 128, get_sfa_ld(m)) or tuple(sfb.shape) != ((n + 127) // 128, k // 128):
+        raise ValueError("scale shape mismatch")
+    _check(lib().dg_k_grouped_fp8_gemm_nt(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(d), _ptr(k_sizes), g, m, n, k,
+                                           _stream()))
     return d
 
 

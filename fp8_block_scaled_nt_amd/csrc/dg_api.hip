@@ -134,6 +134,9 @@ const Config* configs(int* count) {
       make_config<256, 128, 1, 4, 2, dg::kMasked>("masked_256x128_w4_s2"),
       make_config<256, 128, 1, 4, 3, dg::kMasked>("masked_256x128_w4_s3"),
       make_config<64, 64, 1, 4, 3, dg::kMasked>("masked_64x64_w4_s3"),
+      // K-grouped
+      make_config<256, 256, 2, 4, 2, dg::kKGrouped>("kgrouped_256x256_w8_s2"),
+      make_config<128, 128, 2, 2, 2, dg::kKGrouped>("kgrouped_128x128_w4_s2"),
   };
   *count = sizeof(table) / sizeof(table[0]);
   return table;
@@ -412,6 +415,35 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const ui
   p.num_groups = num_groups;
   fill_common(p, *c, max_m, n, k);
   p.num_tiles = num_groups * p.tiles_m * p.tiles_n;
+  return launch(*c, p, p.num_tiles, (hipStream_t)stream);
+}
+
+int dg_k_grouped_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb, uint16_t* d,
+                             const int32_t* k_sizes, int num_groups, int m, int n, int k, dg_stream_t stream) {
+  if (!a || !sfa || !b || !sfb || !d || !k_sizes) return fail(DG_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (m < 0) return fail(DG_ERR_INVALID_ARGUMENT, "m must be >= 0 (got %d)", m);
+  if (num_groups < 0) return fail(DG_ERR_INVALID_ARGUMENT, "num_groups must be >= 0 (got %d)", num_groups);
+  if (int s = check_k_n(n, k)) return s;
+  if (int s = check_rows(m, k)) return s;
+  if ((long long)num_groups * m * n > 0x7FFFFFFFFFFFLL)
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "output too large");
+  if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d) ||
+      (reinterpret_cast<uintptr_t>(k_sizes) & 3u))
+    return fail(DG_ERR_MISALIGNED, "pointers must be 16-byte aligned (k_sizes 4-byte)");
+  if (m == 0 || num_groups == 0) return ok();
+  int dev;
+  DeviceInfo* info;
+  if (int s = current_device(&dev, &info)) return s;
+  const Config* c;
+  if (int s = forced_config(dg::kKGrouped, &c)) return s;
+  if (!c) c = find_config(m <= 256 || n <= 256 ? "kgrouped_128x128_w4_s2" : "kgrouped_256x256_w8_s2", dg::kKGrouped);
+  dg::GemmParams p{};
+  p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.k_sizes = k_sizes;
+  p.num_groups = num_groups;
+  fill_common(p, *c, m, n, k);
+  p.num_tiles = num_groups * p.tiles_m * p.tiles_n;
+  p.splits = 1;
+  p.split_slabs = p.kb_count;
   return launch(*c, p, p.num_tiles, (hipStream_t)stream);
 }
 

@@ -47,7 +47,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) const void* glb_ptr_t;
 
-enum Variant { kDense = 0, kContiguous = 1, kMasked = 2 };
+enum Variant { kDense = 0, kContiguous = 1, kMasked = 2, kKGrouped = 3 };
 
 constexpr int kSlab = 128;        // K bytes per slab (one scale per slab)
 constexpr int kNumXcd = 8;        // MI355X: 8 XCDs, workgroups dealt round-robin
@@ -65,6 +65,7 @@ struct GemmParams {
   uint16_t* d;
   const int32_t* m_indices;  // contiguous layout
   const int32_t* masked_m;   // masked layout
+  const int32_t* k_sizes;    // K-grouped layout: K columns of each group
   int m;                     // rows of A (dense, contiguous) or max_m (masked)
   int n;
   int k;
@@ -263,6 +264,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
     const int r = t - g * per_g;
     tm = r / p.tiles_n;
     tn = r - tm * p.tiles_n;
+  } else if (VAR == kKGrouped) {
+    // groups are consecutive runs of tiles, each run in grouped raster order
+    const int t = xcd_remap(blockIdx.x, gridDim.x);
+    const int per_g = p.tiles_m * p.tiles_n;
+    g = t / per_g;
+    raster(t - g * per_g, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
   } else if (p.splits > 1) {
     tile_id = blockIdx.x / p.splits;
     split = blockIdx.x - tile_id * p.splits;
@@ -309,8 +316,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
     D += (size_t)g * p.m * p.n;
   }
   // K slabs of this workgroup: [kb0, kb0 + KB) (KB is local; p.kb_count is K/128)
-  const int kb0 = split * p.split_slabs;
-  const int KB = p.splits > 1 ? min(p.split_slabs, p.kb_count - kb0) : p.kb_count;
+  int kb0 = split * p.split_slabs;
+  int KB = p.splits > 1 ? min(p.split_slabs, p.kb_count - kb0) : p.kb_count;
+  if (VAR == kKGrouped) {
+    // group g's slabs follow the groups before it; sizes are device values,
+    // so they are clamped here (negative -> 0, whole slabs, inside K)
+    int s0 = 0;
+    for (int h = 0; h < g; ++h) s0 += max(p.k_sizes[h], 0) >> 7;
+    s0 = min(s0, p.kb_count);
+    kb0 = s0;
+    KB = min(max(p.k_sizes[g], 0) >> 7, p.kb_count - s0);
+    D += (size_t)g * p.m * p.n;
+  }
   const int K = p.k;
   // rows worth loading: the masked layout never reads rows past the count
   const int a_rows = VAR == kMasked ? valid_rows : row_limit;

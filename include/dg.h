@@ -110,6 +110,30 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const ui
                                     int num_groups, int max_m, int n, int k, int expected_m,
                                     dg_stream_t stream);
 
+/*
+ * K-grouped GEMM ("DeepGEMM: making LLM matrix multiplication fly",
+ * pomoai.com, core functions: the K-grouped family beside the M-grouped one,
+ * for the irregular shapes of MoE training such as weight gradients, where
+ * the tokens of each expert form a run of K).  The groups are concatenated
+ * along K: group g owns the k_sizes[g] K columns that follow the groups
+ * before it, and
+ *
+ *   D[g][m][n] = bf16( sum over group g's slabs kb of
+ *                      (sum_{k in slab kb} A[m, k] * B[n, k]) * sfa[m, kb] * sfb[n / 128, kb] )
+ *
+ * with the dense layouts and scales for A [m][k], sfa (slab-major,
+ * dg_get_sfa_ld(m)), B [n][k] and sfb [ceil(n/128)][k/128]; D is
+ * [num_groups][m][n] bf16.  k_sizes is device int32 (num_groups entries),
+ * read only on the device so that the call is graph-capturable: each size
+ * must be a multiple of 128 and their sum at most k; on the device a
+ * negative size counts as 0, the remainder below a multiple of 128 is
+ * ignored, and a group is cut off at k.  A group with no K columns gets
+ * D[g] = 0.  Every element of D is written.
+ */
+int dg_k_grouped_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                             uint16_t* d, const int32_t* k_sizes, int num_groups, int m, int n, int k,
+                             dg_stream_t stream);
+
 /* Row alignment required of each expert's segment in the contiguous layout (128). */
 int dg_get_m_alignment_for_contiguous_layout(void);
 

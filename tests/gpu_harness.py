@@ -98,6 +98,21 @@ def run_masked(qa, sa, qb, sb, masked_m, dev, expected_m=0, guard=256):
     return d, flat
 
 
+def run_kgrouped(qa, sa, qb, sb, k_sizes, dev, guard=256):
+    m, k = qa.shape
+    n = qb.shape[0]
+    g = len(k_sizes)
+    a = codes_to_device(qa, dev)
+    b = codes_to_device(qb, dev)
+    sfa = f32_to_device(slab_major(sa), dev)
+    sfb = f32_to_device(sb, dev)
+    ks = torch.from_numpy(np.asarray(k_sizes, np.int32)).to(dev)
+    d, flat = sentinel_bf16((g, m, n), dev, guard)
+    dg.k_grouped_fp8_gemm_nt((a, sfa), (b, sfb), d, ks)
+    torch.cuda.synchronize()
+    return d, flat
+
+
 def guard_untouched(flat, numel):
     tail = flat[numel:].cpu().numpy()
     return bool(np.all(tail == SENTINEL))

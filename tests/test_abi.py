@@ -74,6 +74,17 @@ def test_grouped_validation(lib):
     assert g(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 4, 0, 64, 128, 0, None) == 0
 
 
+def test_k_grouped_validation(lib):
+    f = lib.dg_k_grouped_fp8_gemm_nt
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, None, 2, 64, 64, 256, None) == 1      # null k_sizes
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, -1, 64, 64, 256, None) == 1     # negative group count
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 2, 64, 64, 200, None) == 2      # k not whole slabs
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, P(0x10002), 2, 64, 64, 256, None) == 3  # k_sizes not 4-byte aligned
+    assert f(GOOD, GOOD, GOOD, GOOD, ODD, GOOD, 2, 64, 64, 256, None) == 3       # misaligned d
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 0, 64, 64, 256, None) == 0      # no groups: no-op
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 2, 0, 64, 256, None) == 0       # m = 0: no-op
+
+
 def test_quant_validation(lib):
     assert lib.dg_quantize_a_1x128(None, GOOD, GOOD, 4, 128, None) == 1
     assert lib.dg_quantize_a_1x128(GOOD, GOOD, GOOD, 4, 130, None) == 2

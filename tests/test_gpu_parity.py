@@ -179,3 +179,46 @@ def test_split_k_back_to_back_shapes(gpu, cfg, monkeypatch):
     for splits, (m, n, k) in [("5", (64, 512, 1280)), ("2", (40, 1024, 512)), ("7", (64, 512, 1792))]:
         monkeypatch.setenv("DG_SPLIT_K", splits)
         check_dense(gpu, *dense_case(m, n, k, seed=11), label=f"back-to-back splits={splits}")
+
+
+@pytest.mark.parametrize("cfg", [None, "kgrouped_256x256_w8_s2", "kgrouped_128x128_w4_s2"])
+@pytest.mark.parametrize("m,n,sizes,k_total", [
+    (300, 520, [256, 0, 640, 128], 1280),   # ragged tiles, an empty group, two unused slabs
+    (64, 2112, [1024, 512], 1536),           # skinny M, N with a 64-row partial scale block
+    (520, 300, [128], 128),                  # one group, one slab
+])
+def test_k_grouped(gpu, cfg, m, n, sizes, k_total, monkeypatch):
+    if cfg:
+        monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    x = W.draw_kgrouped(sizes, m, n, seed=m + n + k_total, k_total=k_total)
+    qa, sa = oracle.quantize_a_1x128(x["a"])
+    qb, sb = oracle.quantize_b_128x128(x["b"])
+    print(f"[case] k-grouped {cfg} {m}x{n} sizes={sizes} k={k_total}", flush=True)
+    d, flat = H.run_kgrouped(qa, sa, qb, sb, sizes, gpu)
+    r = oracle.k_grouped_ref(qa, sa, qb, sb, sizes)
+    got = H.d_float(d)
+    for g in range(len(sizes)):
+        if sizes[g] == 0:
+            assert np.all(H.d_bits(d)[g] == 0), "an empty group must be written as +0"
+        else:
+            res = oracle.tolerance_check(got[g], r[g])
+            assert res["ok"], (g, res)
+    assert H.guard_untouched(flat, d.numel())
+
+
+def test_k_grouped_device_side_clamping(gpu):
+    # sizes are device values: negative counts as 0, a remainder below 128
+    # is dropped, and the last group is cut off at K
+    m, n, k_total = 96, 200, 768
+    x = W.draw_kgrouped([k_total], m, n, seed=5)
+    qa, sa = oracle.quantize_a_1x128(x["a"])
+    qb, sb = oracle.quantize_b_128x128(x["b"])
+    print("[case] k-grouped clamping", flush=True)
+    d, flat = H.run_kgrouped(qa, sa, qb, sb, [-128, 300, 1024], gpu)
+    r = oracle.k_grouped_ref(qa, sa, qb, sb, [0, 256, 512])
+    got = H.d_float(d)
+    assert np.all(H.d_bits(d)[0] == 0)
+    for g in (1, 2):
+        res = oracle.tolerance_check(got[g], r[g])
+        assert res["ok"], (g, res)
+    assert H.guard_untouched(flat, d.numel())

@@ -1,4 +1,4 @@
-"""The five named workloads at full size, run the way bench.py runs them:
+"""The named workloads at full size, run the way bench.py runs them:
 fp32 inputs drawn by `workloads`, quantised on the GPU by the library, the
 GEMM with the library's default tile choice.
 
@@ -174,3 +174,42 @@ def test_masked_full(gpu):
             assert np.array_equal(sfb_dev[e, blk], s)
         d_sel = d[e].float()[torch.from_numpy(rows).to(gpu)][:, torch.from_numpy(cols).to(gpu)].cpu().numpy()
         check_sampled(f"{name} expert {e}", d_sel.astype(np.float64), qa_r, sa_r, b_codes, b_scales, rows, cols)
+
+
+def test_kgrouped_full(gpu):
+    name = "kgrouped_4x8192_m4096_n7168"
+    w = W.WORKLOADS[name]
+    m, n = w.shape["m"], w.shape["n"]
+    sizes = list(w.shape["k_sizes"])
+    k = sum(sizes)
+    x = W.draw(name)
+    print(f"[case] {name}: quantise + GEMM on GPU", flush=True)
+    qa, sfa = dg.quantize_a_1x128(H.f32_to_device(x["a"], gpu))
+    qb, sfb = dg.quantize_b_128x128(H.f32_to_device(x["b"], gpu))
+    d, flat = H.sentinel_bf16((len(sizes), m, n), gpu, guard=4096)
+    dg.k_grouped_fp8_gemm_nt((qa, sfa), (qb, sfb), d, torch.from_numpy(x["k_sizes"]).to(gpu))
+    torch.cuda.synchronize()
+    assert H.guard_untouched(flat, d.numel())
+    assert not bool((d.view(torch.int16) == -1).any())  # every element written
+    rng = np.random.default_rng(96)
+    rows = np.unique(np.concatenate([[0, m - 1], pick(rng, m, 8)]))
+    bsel, cols = plan_cols(rng, n, 2, 16)
+    qa_r, sa_r = oracle.quantize_a_1x128(x["a"][rows])
+    assert np.array_equal(qa.view(torch.uint8)[torch.from_numpy(rows).to(gpu)].cpu().numpy(), qa_r)
+    b_codes = np.zeros((len(cols), k), np.uint8)
+    b_scales = np.zeros((len(cols), k // 128), np.float32)
+    sfb_dev = sfb.cpu().numpy()
+    for blk in bsel:
+        lo, hi, q, s = oracle_b_block(x["b"], blk)
+        sel = (cols >= lo) & (cols < hi)
+        b_codes[sel] = q[cols[sel] - lo]
+        b_scales[sel] = s
+        assert np.array_equal(sfb_dev[blk], s)
+    s0 = 0
+    for g, size in enumerate(sizes):
+        s1 = s0 + size // 128
+        kc = slice(s0 * 128, s1 * 128)
+        d_sel = d[g].float()[torch.from_numpy(rows).to(gpu)][:, torch.from_numpy(cols).to(gpu)].cpu().numpy()
+        check_sampled(f"{name} group {g}", d_sel.astype(np.float64), qa_r[:, kc], sa_r[:, s0:s1],
+                      b_codes[:, kc], b_scales[:, s0:s1], rows, cols)
+        s0 = s1

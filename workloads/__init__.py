@@ -23,7 +23,7 @@ class Workload:
 
     def __init__(self, name, kind, desc, **shape):
         self.name = name
-        self.kind = kind  # "dense" | "contiguous" | "masked"
+        self.kind = kind  # "dense" | "contiguous" | "masked" | "kgrouped"
         self.desc = desc
         self.shape = shape
 
@@ -49,6 +49,12 @@ WORKLOADS = {
         "moe_masked_16x256_n4096_k7168", "masked",
         "MoE grouped masked decode, 16 experts, max_m=256, N=4096 K=7168",
         g=16, max_m=256, n=4096, k=7168, b_std=0.02),
+    # K-grouped (MoE weight-gradient shape): 4 experts' 8192 tokens each on K,
+    # M and N the expert FFN's output and input widths of the MoE shapes above
+    "kgrouped_4x8192_m4096_n7168": Workload(
+        "kgrouped_4x8192_m4096_n7168", "kgrouped",
+        "K-grouped GEMM, 4 groups x 8192 K columns, M=4096 N=7168",
+        k_sizes=(8192, 8192, 8192, 8192), m=4096, n=7168, b_std=1.0),
 }
 
 
@@ -105,6 +111,17 @@ def draw_masked(g, max_m, n, k, seed=0, b_std=0.02, masked_m=None):
     return {"a": a, "b": b, "masked_m": masked_m}
 
 
+def draw_kgrouped(k_sizes, m, n, seed=0, b_std=1.0, k_total=None):
+    """A (m x K) ~ N(0,1) then B (n x K) ~ N(0, b_std^2), K = k_total or the
+    sum of the group sizes (both operands hold activation-like data: output
+    gradients and layer inputs, tokens along K)."""
+    rng = np.random.default_rng(seed)
+    k = int(sum(k_sizes)) if k_total is None else int(k_total)
+    a = _normal(rng, (m, k), 1.0)
+    b = _normal(rng, (n, k), b_std)
+    return {"a": a, "b": b, "k_sizes": np.asarray(k_sizes, dtype=np.int32)}
+
+
 def draw(name, seed=0):
     """Draw the named workload's inputs with its recipe."""
     w = WORKLOADS[name]
@@ -113,6 +130,8 @@ def draw(name, seed=0):
         return draw_dense(s["m"], s["n"], s["k"], seed, s["b_std"])
     if w.kind == "contiguous":
         return draw_contiguous(s["group_rows"], s["n"], s["k"], seed, s["b_std"])
+    if w.kind == "kgrouped":
+        return draw_kgrouped(s["k_sizes"], s["m"], s["n"], seed, s["b_std"])
     return draw_masked(s["g"], s["max_m"], s["n"], s["k"], seed, s["b_std"])
 
 
@@ -144,6 +163,15 @@ def algorithmic_work(kind, **p):
         rows = int(cnt.sum())
         experts = int((cnt > 0).sum())
         index_bytes = 4 * cnt.size
+    elif kind == "kgrouped":
+        # every group reads its own K columns of A and B once and writes a
+        # full M x N result (zeros for an empty group)
+        sizes = np.maximum(np.asarray(p["k_sizes"], np.int64), 0)
+        m, kk, g = p["m"], int(sizes.sum()), sizes.size
+        kbb = kk // SLAB
+        flops = 2.0 * m * n * kk
+        nbytes = m * kk + 4 * m * kbb + n * kk + 4 * nb * kbb + 4 * g + 2 * g * m * n
+        return flops, nbytes
     else:
         raise ValueError(kind)
     flops = 2.0 * rows * n * k
@@ -162,5 +190,7 @@ def workload_work(name, inputs=None):
     if w.kind == "contiguous":
         mi = inputs["m_indices"] if inputs is not None else contiguous_indices(s["group_rows"])
         return algorithmic_work("contiguous", m_indices=mi, g=len(s["group_rows"]), n=s["n"], k=s["k"])
+    if w.kind == "kgrouped":
+        return algorithmic_work("kgrouped", k_sizes=s["k_sizes"], m=s["m"], n=s["n"], k=int(sum(s["k_sizes"])))
     mm = inputs["masked_m"] if inputs is not None else np.random.default_rng(0).integers(0, s["max_m"] + 1, s["g"])
     return algorithmic_work("masked", masked_m=mm, max_m=s["max_m"], n=s["n"], k=s["k"])
