@@ -25,7 +25,8 @@ Modules
 -------
 e4m3   exact 256-entry decode table, round-to-nearest-even saturating encoder
 quant  1x128 (activation) and 128x128 (weight) quantisers
-gemm   dense, contiguous-grouped, masked-grouped and K-grouped reference GEMMs in fp64
+gemm   dense, contiguous-grouped, masked-grouped and K-grouped reference GEMMs in fp64,
+       and the BF16 NT GEMM
 check  the element-wise acceptance rule
 """
 
@@ -38,5 +39,7 @@ from .gemm import (  # noqa: F401
     grouped_masked_ref,
     k_grouped_ref,
     k_grouped_ref_at,
+    bf16_gemm_nt_ref,
+    bf16_to_f64,
 )
 from .check import tolerance_check, bf16_bits_to_float, bf16_round  # noqa: F401

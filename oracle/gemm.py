@@ -235,3 +235,24 @@ def k_grouped_ref_at(qa, sfa, qb, sfb, k_sizes, groups, rows, cols):
             rr, cc = rows[sel], cols[sel]
             out[sel] = _entries(qa[rr, kc], sa[rr, s0:s1], qb[cc, kc], sb[cc // SLAB, s0:s1])
     return out
+
+
+def bf16_to_f64(bits):
+    """bf16 bit patterns (uint16) to float64, exactly: a bf16 value is the
+    upper half of the fp32 with the same bits."""
+    b = np.asarray(bits, np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def bf16_gemm_nt_ref(a_bits, b_bits):
+    """BF16 NT GEMM reference: D = A . B^T for bf16 A (M x K) and B (N x K),
+    given as uint16 bit patterns, in fp64 (the BF16 family named on
+    "DeepGEMM: making LLM matrix multiplication fly", pomoai.com, core
+    functions).  No scales: bf16 keeps an 8-bit exponent, so the pages'
+    fine-grained scaling is an FP8 device.  Each product of two bf16 values
+    is exact in fp64 (8-bit significands); the sum over K is rounded to fp64."""
+    a = bf16_to_f64(a_bits)
+    b = bf16_to_f64(b_bits)
+    if a.shape[1] != b.shape[1]:
+        raise ValueError("A and B must share K")
+    return a @ b.T

@@ -11,7 +11,9 @@
   padding rows and rows past masked_m have no result, masked_m is clamped;
 * the K-grouped layout against the brute force on each group's K columns,
   its groups summing to the dense result, unit scales giving a plain matmul
-  per K slice, an empty group giving zero, and bad group sizes rejected.
+  per K slice, an empty group giving zero, and bad group sizes rejected;
+* the BF16 GEMM: its bf16 decode against torch's, exact-rational brute force,
+  and closed forms (ones give K, a one-hot row selects a column of B).
 """
 
 from fractions import Fraction
@@ -21,7 +23,8 @@ import pytest
 import torch
 
 from oracle import (gemm_nt_ref, gemm_nt_ref_at, grouped_contiguous_ref,
-                    grouped_masked_ref, k_grouped_ref, k_grouped_ref_at, tolerance_check)
+                    grouped_masked_ref, k_grouped_ref, k_grouped_ref_at, tolerance_check,
+                    bf16_gemm_nt_ref, bf16_to_f64)
 from oracle.gemm import grouped_contiguous_ref_at, grouped_masked_ref_at
 
 SPECIAL = np.array([0x7E, 0xFE, 0x01, 0x81, 0x00, 0x80, 0x07, 0x08, 0x38, 0x5F], dtype=np.uint8)
@@ -289,3 +292,45 @@ def test_k_grouped_at_matches_full_and_rejects_bad_sizes():
     for bad in ([100], [-128], [512, 256]):
         with pytest.raises(ValueError):
             k_grouped_ref(qa, sa, qb, sb, bad)
+
+
+
+# ---- BF16 NT GEMM
+
+def _bf16_bits_from_torch(x):
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_bf16_decode_matches_library():
+    rng = np.random.default_rng(31)
+    bits = rng.integers(0, 1 << 16, 4096).astype(np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]  # no inf / NaN
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(bf16_to_f64(bits), ref)
+
+
+def test_bf16_gemm_against_brute_force():
+    rng = np.random.default_rng(32)
+    m, n, k = 3, 4, 64
+    a = _bf16_bits_from_torch(rng.standard_normal((m, k)).astype(np.float32) * 3)
+    b = _bf16_bits_from_torch(rng.standard_normal((n, k)).astype(np.float32))
+    got = bf16_gemm_nt_ref(a, b)
+    ta = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    tb = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    for i in range(m):
+        for j in range(n):
+            exact = sum(Fraction(ta[i, kk]) * Fraction(tb[j, kk]) for kk in range(k))
+            mag = sum(abs(ta[i, kk] * tb[j, kk]) for kk in range(k))
+            assert abs(Fraction(float(got[i, j])) - exact) <= Fraction(k * 2.0 ** -53 * mag)
+
+
+def test_bf16_gemm_closed_forms():
+    # ones give K; a one-hot row of A picks the matching column of B
+    k = 256
+    one = np.full((2, k), 0x3F80, np.uint16)
+    assert np.all(bf16_gemm_nt_ref(one, one) == k)
+    rng = np.random.default_rng(33)
+    b = _bf16_bits_from_torch(rng.standard_normal((5, k)).astype(np.float32))
+    a = np.zeros((1, k), np.uint16)
+    a[0, 17] = 0x3F80
+    assert np.array_equal(bf16_gemm_nt_ref(a, b)[0], bf16_to_f64(b[:, 17]))

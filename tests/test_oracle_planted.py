@@ -41,6 +41,9 @@ MUTATIONS = [
     ("gemm.py", "starts = ends - sizes", "starts = ends - sizes + SLAB * (sizes > 0)"),
     ("gemm.py", "np.asarray(sfa)[:, s0:s1], qb[:, cols]", "np.asarray(sfa)[:, 0:s1 - s0], qb[:, cols]"),
     ("gemm.py", "if np.any(sizes < 0) or np.any(sizes % SLAB):", "if np.any(sizes < 0):"),
+    # BF16: wrong half of the fp32 word, transposed operand
+    ("gemm.py", "b = np.asarray(bits, np.uint16).astype(np.uint32) << 16", "b = np.asarray(bits, np.uint16).astype(np.uint32) << 15"),
+    ("gemm.py", "    return a @ b.T\n", "    return a @ b[::-1].T\n"),
     # e4m3: tie rule, exponent bias, saturation code, subnormal boundary
     ("e4m3.py", "q = np.rint(steps)", "q = np.floor(steps + 0.5)"),
     ("e4m3.py", "mag = (8 + f) * 2.0 ** (e - 10)", "mag = (8 + f) * 2.0 ** (e - 9)"),
