@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16 MFMA
 ROTATE_BYTES = 600 << 20       # > 2x the 256 MiB Infinity Cache
 MAIN_WORKLOAD = "dense_decode_64x2112x7168"
 CALIB_BYTES = 1 << 30          # plain-kernel traffic for the counter calibration
@@ -163,6 +164,23 @@ def setup_workload(torch, np, dg, W, name, dev):
             dg.m_grouped_fp8_gemm_nt_contiguous((st["qa"], st["sfa"]), (st["qb"], st["sfb"]), st["d"], st["idx"])
 
         return w.kind, dict(m_indices=inp["m_indices"], g=len(s["group_rows"]), n=n, k=k), rot, launch, None, inp
+    if w.kind == "bf16":
+        m, n, k = s["m"], s["n"], s["k"]
+        a16 = torch.from_numpy(inp["a"]).to(dev).to(torch.bfloat16)
+        b16 = torch.from_numpy(inp["b"]).to(dev).to(torch.bfloat16)
+
+        def make(i):
+            d = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            if i == 0:
+                return {"a": a16, "b": b16, "d": d}
+            return {"a": a16.clone(), "b": b16.clone(), "d": d}
+
+        rot = Rotation(make, 2 * (m * k + n * k + m * n))
+
+        def launch(st):
+            dg.bf16_gemm_nt(st["a"], st["b"], st["d"])
+
+        return w.kind, dict(m=m, n=n, k=k), rot, launch, None, inp
     if w.kind == "kgrouped":
         m, n = s["m"], s["n"]
         ks = torch.from_numpy(inp["k_sizes"]).to(dev)
@@ -316,10 +334,12 @@ def main():
         a_us, md_us = kernel_time_us(torch, dg, launch_x, rot_x, max(10, args.kernel_launches // 4))
         tf = fl / (a_us * 1e-6) / 1e12
         gbs = by / (a_us * 1e-6) / 1e9
-        bound = "mfma" if fl / by > FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
+        peak_tf = BF16_PEAK_TFLOPS if kind_x == "bf16" else FP8_PEAK_TFLOPS
+        bound = "mfma" if fl / by > peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
         extra[name] = {"kernel_avg_us": round(a_us, 2), "kernel_median_us": round(md_us, 2),
                        "tflops": round(tf, 1), "gbs": round(gbs, 1), "bound": bound,
-                       "frac": round(tf / FP8_PEAK_TFLOPS if bound == "mfma" else gbs / HBM_PEAK_GBS, 4),
+                       "peak": peak_tf if bound == "mfma" else HBM_PEAK_GBS,
+                       "frac": round(tf / peak_tf if bound == "mfma" else gbs / HBM_PEAK_GBS, 4),
                        "algorithmic_flops": fl, "algorithmic_bytes": by}
         print(f"[bench] {name}: {a_us:.1f} us, {tf:.1f} TFLOP/s, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
         del rot_x, inp_x

@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_PKG_DIR, "libdg.so")
 __all__ = [
     "DGError", "lib", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous",
     "m_grouped_fp8_gemm_nt_masked", "quantize_a_1x128", "quantize_b_128x128",
-    "k_grouped_fp8_gemm_nt", "get_m_alignment_for_contiguous_layout", "get_sfa_ld", "empty_sfa",
+    "k_grouped_fp8_gemm_nt", "bf16_gemm_nt", "get_m_alignment_for_contiguous_layout", "get_sfa_ld", "empty_sfa",
     "profile_next_launch",
     "reserve_workspace",
 ]
@@ -46,6 +46,7 @@ _SIGNATURES = {
     "dg_m_grouped_fp8_gemm_nt_contiguous": [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _vp],
     "dg_m_grouped_fp8_gemm_nt_masked": [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _vp],
     "dg_k_grouped_fp8_gemm_nt": [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _vp],
+    "dg_bf16_gemm_nt": [_vp, _vp, _vp, _ci, _ci, _ci, _vp],
     "dg_get_m_alignment_for_contiguous_layout": [],
     "dg_get_sfa_ld": [_ci],
     "dg_quantize_a_1x128": [_vp, _vp, _vp, _ci, _ci, _vp],
@@ -218,6 +219,19 @@ def k_grouped_fp8_gemm_nt(a_pair, b_pair, d, k_sizes):
         raise ValueError("scale shape mismatch")
     _check(lib().dg_k_grouped_fp8_gemm_nt(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(d), _ptr(k_sizes), g, m, n, k,
                                            _stream()))
+    return d
+
+
+def bf16_gemm_nt(a, b, d):
+    """BF16 NT GEMM: d (bf16 [m, n]) = a (bf16 [m, k]) . b (bf16 [n, k])^T, in place."""
+    _need(a, "a", (torch.bfloat16,), 2)
+    _need(b, "b", (torch.bfloat16,), 2)
+    _need(d, "d", (torch.bfloat16,), 2)
+    m, k = a.shape
+    n = b.shape[0]
+    if b.shape[1] != k or tuple(d.shape) != (m, n):
+        raise ValueError(f"shape mismatch a{tuple(a.shape)} b{tuple(b.shape)} d{tuple(d.shape)}")
+    _check(lib().dg_bf16_gemm_nt(_ptr(a), _ptr(b), _ptr(d), m, n, k, _stream()))
     return d
 
 

@@ -89,16 +89,16 @@ int current_device(int* dev, DeviceInfo** info) {
 // ---- tile configurations (compile-time instantiations; the host picks one)
 struct Config {
   const char* name;
-  int variant, bm, bn, wm, wn, nst, sched;
+  int variant, bm, bn, wm, wn, nst, sched, dtype;
   const void* fn;
   int smem;
   int threads() const { return wm * wn * 64; }
 };
 
-template <int BM, int BN, int WM, int WN, int NST, int VAR, int SCHED = dg::kInterleaved>
+template <int BM, int BN, int WM, int WN, int NST, int VAR, int SCHED = dg::kInterleaved, int DT = dg::kFp8>
 Config make_config(const char* name) {
-  return Config{name, VAR, BM, BN, WM, WN, NST, SCHED,
-                reinterpret_cast<const void*>(&dg::gemm_fp8_nt_kernel<BM, BN, WM, WN, NST, VAR, SCHED>),
+  return Config{name, VAR, BM, BN, WM, WN, NST, SCHED, DT,
+                reinterpret_cast<const void*>(&dg::gemm_fp8_nt_kernel<BM, BN, WM, WN, NST, VAR, SCHED, DT>),
                 dg::Smem<BM, BN, NST>::kBytes};
 }
 
@@ -137,22 +137,27 @@ const Config* configs(int* count) {
       // K-grouped
       make_config<256, 256, 2, 4, 2, dg::kKGrouped>("kgrouped_256x256_w8_s2"),
       make_config<128, 128, 2, 2, 2, dg::kKGrouped>("kgrouped_128x128_w4_s2"),
+      // BF16 dense (the variant tag is kBf16Dense so that DG_FORCE_CONFIG
+      // names pick among these only)
+      make_config<256, 256, 2, 4, 2, dg::kDense, dg::kInterleaved, dg::kBf16>("bf16_256x256_w8_s2"),
+      make_config<128, 128, 2, 2, 2, dg::kDense, dg::kInterleaved, dg::kBf16>("bf16_128x128_w4_s2"),
+      make_config<64, 32, 2, 2, 4, dg::kDense, dg::kInterleaved, dg::kBf16>("bf16_64x32_w4_s4"),
   };
   *count = sizeof(table) / sizeof(table[0]);
   return table;
 }
 
-const Config* find_config(const char* name, int variant) {
+const Config* find_config(const char* name, int variant, int dtype = dg::kFp8) {
   int cnt = 0;
   const Config* t = configs(&cnt);
   for (int i = 0; i < cnt; ++i)
-    if (t[i].variant == variant && strcmp(t[i].name, name) == 0) return &t[i];
+    if (t[i].variant == variant && t[i].dtype == dtype && strcmp(t[i].name, name) == 0) return &t[i];
   return nullptr;
 }
 
 // DG_FORCE_CONFIG=<name> pins the configuration of the variant it names (for
 // tuning sweeps); an unknown name is an error rather than silently ignored.
-int forced_config(int variant, const Config** out) {
+int forced_config(int variant, const Config** out, int dtype = dg::kFp8) {
   *out = nullptr;
   const char* e = getenv("DG_FORCE_CONFIG");
   if (!e || !*e) return DG_OK;
@@ -161,7 +166,7 @@ int forced_config(int variant, const Config** out) {
   bool known = false;
   for (int i = 0; i < cnt; ++i) known = known || strcmp(t[i].name, e) == 0;
   if (!known) return fail(DG_ERR_INVALID_ARGUMENT, "DG_FORCE_CONFIG names no configuration: %s", e);
-  *out = find_config(e, variant);
+  *out = find_config(e, variant, dtype);
   return DG_OK;
 }
 
@@ -263,6 +268,45 @@ int check_rows(long long rows, int k) {
   return DG_OK;
 }
 
+// Dense launch with the split-K choice, shared by the fp8 and bf16 entry
+// points; k_bytes is K in bytes (one per fp8 value, two per bf16 value).
+int launch_dense(const Config* c, dg::GemmParams& p, int dev, const DeviceInfo* info, int m, int n, int k_bytes,
+                 dg_stream_t stream) {
+  p.num_groups = 1;
+  fill_common(p, *c, m, n, k_bytes);
+  p.num_tiles = p.tiles_m * p.tiles_n;
+  p.splits = 1;
+  p.split_slabs = p.kb_count;
+  // Split K over workgroups when the tiles alone cannot fill the GPU (skinny
+  // M).  Decode-shaped calls are bound by HBM latency more than by bandwidth,
+  // so about two workgroups per CU (every small-tile configuration fits two)
+  // keep more loads in flight than one; measured on 64 x 2112 x 7168, six
+  // splits of 64 x 32 tiles beat one workgroup per CU by ~15%.
+  int splits = 1;
+  if (const char* e = getenv("DG_SPLIT_K")) splits = atoi(e);
+  else if (c->sched == dg::kInterleaved && p.num_tiles * 2 <= info->cus && p.kb_count >= 4) {
+    splits = 2 * info->cus / p.num_tiles - 1;
+    const int min_split_slabs = 2;
+    if (splits > p.kb_count / min_split_slabs) splits = p.kb_count / min_split_slabs;
+    if (splits > 8) splits = 8;  // the reducer reads up to 8 partials per batch
+  }
+  if (splits > 1) {
+    const int per = (p.kb_count + splits - 1) / splits;
+    splits = (p.kb_count + per - 1) / per;  // no empty splits
+    p.splits = splits;
+    p.split_slabs = per;
+  }
+  if (p.splits > 1) {
+    if (c->sched != dg::kInterleaved)
+      return fail(DG_ERR_INVALID_ARGUMENT, "configuration %s does not support split-K", c->name);
+    if ((size_t)p.num_tiles > kCounterInts)
+      return fail(DG_ERR_UNSUPPORTED_SHAPE, "too many tiles for split-K (%d)", p.num_tiles);
+    const size_t part = (size_t)p.num_tiles * p.splits * c->bm * c->bn * sizeof(float);
+    if (int s = ensure_workspace(dev, part, &p.ws_partial, &p.ws_count)) return s;
+  }
+  return launch(*c, p, p.num_tiles * p.splits, (hipStream_t)stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -325,39 +369,34 @@ int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const f
   }
   dg::GemmParams p{};
   p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d;
-  p.num_groups = 1;
-  fill_common(p, *c, m, n, k);
-  p.num_tiles = p.tiles_m * p.tiles_n;
-  p.splits = 1;
-  p.split_slabs = p.kb_count;
-  // Split K over workgroups when the tiles alone cannot fill the GPU (skinny
-  // M).  Decode-shaped calls are bound by HBM latency more than by bandwidth,
-  // so about two workgroups per CU (every small-tile configuration fits two)
-  // keep more loads in flight than one; measured on 64 x 2112 x 7168, six
-  // splits of 64 x 32 tiles beat one workgroup per CU by ~15%.
-  int splits = 1;
-  if (const char* e = getenv("DG_SPLIT_K")) splits = atoi(e);
-  else if (c->sched == dg::kInterleaved && p.num_tiles * 2 <= info->cus && p.kb_count >= 4) {
-    splits = 2 * info->cus / p.num_tiles - 1;
-    const int min_split_slabs = 2;
-    if (splits > p.kb_count / min_split_slabs) splits = p.kb_count / min_split_slabs;
-    if (splits > 8) splits = 8;  // the reducer reads up to 8 partials per batch
+  return launch_dense(c, p, dev, info, m, n, k, stream);
+}
+
+int dg_bf16_gemm_nt(const uint16_t* a, const uint16_t* b, uint16_t* d, int m, int n, int k, dg_stream_t stream) {
+  if (!a || !b || !d) return fail(DG_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (m < 0) return fail(DG_ERR_INVALID_ARGUMENT, "m must be >= 0 (got %d)", m);
+  if (n < 1) return fail(DG_ERR_INVALID_ARGUMENT, "n must be >= 1 (got %d)", n);
+  if (k < 64 || k % 64 != 0 || k > (1 << 30))
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "k must be a positive multiple of 64 (got %d)", k);
+  if (int s = check_k_n(n, 2 * k)) return s;
+  if (int s = check_rows(m, 2 * k)) return s;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(d)) return fail(DG_ERR_MISALIGNED, "pointers must be 16-byte aligned");
+  if (m == 0) return ok();
+  int dev;
+  DeviceInfo* info;
+  if (int s = current_device(&dev, &info)) return s;
+  const Config* c;
+  if (int s = forced_config(dg::kDense, &c, dg::kBf16)) return s;
+  if (!c) {
+    if (m <= 64) c = find_config("bf16_64x32_w4_s4", dg::kDense, dg::kBf16);
+    else if (m <= 256 || n <= 256) c = find_config("bf16_128x128_w4_s2", dg::kDense, dg::kBf16);
+    else c = find_config("bf16_256x256_w8_s2", dg::kDense, dg::kBf16);
   }
-  if (splits > 1) {
-    const int per = (p.kb_count + splits - 1) / splits;
-    splits = (p.kb_count + per - 1) / per;  // no empty splits
-    p.splits = splits;
-    p.split_slabs = per;
-  }
-  if (p.splits > 1) {
-    if (c->sched != dg::kInterleaved)
-      return fail(DG_ERR_INVALID_ARGUMENT, "configuration %s does not support split-K", c->name);
-    if ((size_t)p.num_tiles > kCounterInts)
-      return fail(DG_ERR_UNSUPPORTED_SHAPE, "too many tiles for split-K (%d)", p.num_tiles);
-    const size_t part = (size_t)p.num_tiles * p.splits * c->bm * c->bn * sizeof(float);
-    if (int s = ensure_workspace(dev, part, &p.ws_partial, &p.ws_count)) return s;
-  }
-  return launch(*c, p, p.num_tiles * p.splits, (hipStream_t)stream);
+  dg::GemmParams p{};
+  p.a = reinterpret_cast<const uint8_t*>(a);
+  p.b = reinterpret_cast<const uint8_t*>(b);
+  p.d = d;
+  return launch_dense(c, p, dev, info, m, n, 2 * k, stream);
 }
 
 int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b,

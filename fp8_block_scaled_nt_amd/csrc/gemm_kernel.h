@@ -48,6 +48,10 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) const void* glb_ptr_t;
 
 enum Variant { kDense = 0, kContiguous = 1, kMasked = 2, kKGrouped = 3 };
+// Operand type: e4m3 with block scales, or bf16 without scales (a 128-byte
+// slab row then holds 64 K values).
+enum DType { kFp8 = 0, kBf16 = 1 };
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kSlab = 128;        // K bytes per slab (one scale per slab)
 constexpr int kNumXcd = 8;        // MI355X: 8 XCDs, workgroups dealt round-robin
@@ -231,7 +235,7 @@ __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 // groups that alternate load and compute steps, see below).
 enum Schedule { kInterleaved = 0, kPingPong = 1 };
 
-template <int BM, int BN, int WM, int WN, int NST, int VAR, int SCHED = kInterleaved>
+template <int BM, int BN, int WM, int WN, int NST, int VAR, int SCHED = kInterleaved, int DT = kFp8>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p) {
   constexpr int kThreads = WM * WN * 64;
   constexpr int kWaves = WM * WN;
@@ -388,7 +392,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
     blk = blk < p.nb_count ? blk : p.nb_count - 1;
     sb_off = (uint32_t)blk * (uint32_t)p.kb_count;  // sfb row stride: all K slabs
   }
-  const int c_loads = a_live + b_live + 2;
+  const int c_loads = a_live + b_live + (DT == kFp8 ? 2 : 0);
 
   // Buffer descriptors of this tile's operands (sizes in bytes; the host
   // keeps every operand below 4 GiB).
@@ -398,7 +402,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   const v4i_rsrc rs_sb = make_rsrc(SFB, (uint32_t)p.nb_count * (uint32_t)p.kb_count * 4u);
   // DMA instruction d (0 .. kNumDma-1) of this wave for slab kl into stage
   // buf: the A rows, then the B rows, then the two scale loads.
-  constexpr int kNumDma = kPerWaveA + kPerWaveB + 2;
+  constexpr int kScaleDma = DT == kFp8 ? 2 : 0;  // bf16 operands carry no scales
+  constexpr int kNumDma = kPerWaveA + kPerWaveB + kScaleDma;
   auto issue_one = [&](int kl, int buf, int d) {
     const int kb = kb0 + kl;  // global slab index
     uint8_t* st = smem + buf * S::kStage;
@@ -469,6 +474,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
     // step ends with lgkmcnt(0), so no LDS read is in flight when a stage is
     // refilled.
     static_assert(BM == 256 && BN == 256 && WM == 2 && WN == 4 && NST == 2, "ping-pong tile shape");
+    static_assert(DT == kFp8, "ping-pong schedule is written for fp8 operands");
     static_assert(kSbUniform, "a wave's columns must share one B scale block");
     constexpr int kFh = 4;          // A fragments per chunk
     constexpr int kNch = FM / kFh;  // chunks per slab
@@ -619,7 +625,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
 
       float sbv[FN];
       #pragma unroll
-      for (int j = 0; j < FN; ++j) sbv[j] = sSb[kSbUniform ? sb_idx[0] : sb_idx[j]];
+      for (int j = 0; j < FN; ++j) sbv[j] = DT == kFp8 ? sSb[kSbUniform ? sb_idx[0] : sb_idx[j]] : 0.f;
 
       v8i bf[FN];
       #pragma unroll
@@ -647,11 +653,33 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
         const v4i lo = *(const v4i*)(sA + f * 2048 + frag_lo);
         const v4i hi = *(const v4i*)(sA + f * 2048 + frag_hi);
         abuf[i % kAbuf] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        sabuf[i % kSabuf] = *(const v4f*)(sSa + wm * TM + i * 16 + 4 * (lane >> 4));
+        if constexpr (DT == kFp8) sabuf[i % kSabuf] = *(const v4f*)(sSa + wm * TM + i * 16 + 4 * (lane >> 4));
       };
       #pragma unroll
       for (int i = 0; i < kPf; ++i)
         if (VAR != kMasked || i < fm_valid) load_a(i);
+      if constexpr (DT == kBf16) {
+        // bf16: a slab row is 64 K values; the fragment read's low half
+        // feeds one K=32 MFMA and its high half a second one, accumulating
+        // in place (no scales, no promotion).  All low-half MFMAs of an A
+        // fragment come before the high-half ones, so each MFMA's
+        // predecessor on the same accumulator is FN-1 MFMAs back.
+        auto lo8 = [](const v8i& x) { return __builtin_bit_cast(v8bf, v4i{x[0], x[1], x[2], x[3]}); };
+        auto hi8 = [](const v8i& x) { return __builtin_bit_cast(v8bf, v4i{x[4], x[5], x[6], x[7]}); };
+        #pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          if (VAR == kMasked && i >= fm_valid) continue;
+          if (i + kPf < FM && (VAR != kMasked || i + kPf < fm_valid)) load_a(i + kPf);
+          #pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo8(abuf[i % kAbuf]), lo8(bf[j]), acc[i][j], 0, 0, 0);
+          #pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi8(abuf[i % kAbuf]), hi8(bf[j]), acc[i][j], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        continue;
+      }
       #pragma unroll
       for (int t = 0; t < F + kLag; ++t) {
         if (t < F) {

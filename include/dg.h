@@ -111,6 +111,18 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const ui
                                     dg_stream_t stream);
 
 /*
+ * BF16 NT GEMM: D[m][n] = bf16( sum_k A[m, k] * B[n, k] ) for bf16 A [m][k]
+ * and B [n][k] (bit patterns in uint16), fp32 accumulation, no scales
+ * ("DeepGEMM: making LLM matrix multiplication fly", pomoai.com, core
+ * functions: BF16 GEMMs beside the FP8 ones).  The same tiles, LDS layout and
+ * split-K as the FP8 dense GEMM run it on gfx950's bf16 MFMA
+ * (v_mfma_f32_16x16x32_bf16).  k must be a positive multiple of 64 (one
+ * 128-byte slab row); otherwise as dg_fp8_gemm_nt (m may be 0, n >= 1,
+ * 16-byte aligned pointers, the split-K workspace note applies).
+ */
+int dg_bf16_gemm_nt(const uint16_t* a, const uint16_t* b, uint16_t* d, int m, int n, int k, dg_stream_t stream);
+
+/*
  * K-grouped GEMM ("DeepGEMM: making LLM matrix multiplication fly",
  * pomoai.com, core functions: the K-grouped family beside the M-grouped one,
  * for the irregular shapes of MoE training such as weight gradients, where

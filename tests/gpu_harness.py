@@ -113,6 +113,17 @@ def run_kgrouped(qa, sa, qb, sb, k_sizes, dev, guard=256):
     return d, flat
 
 
+def run_bf16(a_bits, b_bits, dev, guard=256):
+    m, k = a_bits.shape
+    n = b_bits.shape[0]
+    a = torch.from_numpy(np.ascontiguousarray(a_bits).view(np.int16)).to(dev).view(torch.bfloat16)
+    b = torch.from_numpy(np.ascontiguousarray(b_bits).view(np.int16)).to(dev).view(torch.bfloat16)
+    d, flat = sentinel_bf16((m, n), dev, guard)
+    dg.bf16_gemm_nt(a, b, d)
+    torch.cuda.synchronize()
+    return d, flat
+
+
 def guard_untouched(flat, numel):
     tail = flat[numel:].cpu().numpy()
     return bool(np.all(tail == SENTINEL))

@@ -85,6 +85,15 @@ def test_k_grouped_validation(lib):
     assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 2, 0, 64, 256, None) == 0       # m = 0: no-op
 
 
+def test_bf16_validation(lib):
+    f = lib.dg_bf16_gemm_nt
+    assert f(None, GOOD, GOOD, 64, 64, 128, None) == 1      # null a
+    assert f(GOOD, GOOD, GOOD, -1, 64, 128, None) == 1      # negative m
+    assert f(GOOD, GOOD, GOOD, 64, 64, 96, None) == 2       # k not a multiple of 64
+    assert f(GOOD, GOOD, ODD, 64, 64, 128, None) == 3       # misaligned d
+    assert f(GOOD, GOOD, GOOD, 0, 64, 128, None) == 0       # m = 0: no-op
+
+
 def test_quant_validation(lib):
     assert lib.dg_quantize_a_1x128(None, GOOD, GOOD, 4, 128, None) == 1
     assert lib.dg_quantize_a_1x128(GOOD, GOOD, GOOD, 4, 130, None) == 2

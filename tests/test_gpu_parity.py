@@ -222,3 +222,38 @@ def test_k_grouped_device_side_clamping(gpu):
         res = oracle.tolerance_check(got[g], r[g])
         assert res["ok"], (g, res)
     assert H.guard_untouched(flat, d.numel())
+
+
+
+def bf16_bits(x):
+    import torch
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("cfg", [None, "bf16_256x256_w8_s2", "bf16_128x128_w4_s2", "bf16_64x32_w4_s4"])
+@pytest.mark.parametrize("m,n,k", [(300, 520, 640), (64, 2112, 1024), (1, 16, 64), (520, 300, 128)])
+def test_bf16_gemm(gpu, cfg, m, n, k, monkeypatch):
+    if cfg:
+        monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    x = W.draw_dense(m, n, k, seed=m + 2 * n + k)
+    a, b = bf16_bits(x["a"]), bf16_bits(x["b"])
+    print(f"[case] bf16 {cfg} {m}x{n}x{k}", flush=True)
+    d, flat = H.run_bf16(a, b, gpu)
+    r = oracle.bf16_gemm_nt_ref(a, b)
+    res = oracle.tolerance_check(H.d_float(d), r)
+    assert res["ok"], res
+    assert H.guard_untouched(flat, d.numel())
+
+
+def test_bf16_gemm_forced_split_k(gpu, monkeypatch):
+    monkeypatch.setenv("DG_FORCE_CONFIG", "bf16_64x32_w4_s4")
+    monkeypatch.setenv("DG_SPLIT_K", "5")
+    m, n, k = 48, 200, 1280
+    x = W.draw_dense(m, n, k, seed=3)
+    a, b = bf16_bits(x["a"]), bf16_bits(x["b"])
+    print("[case] bf16 split-K 5", flush=True)
+    d, flat = H.run_bf16(a, b, gpu)
+    res = oracle.tolerance_check(H.d_float(d), oracle.bf16_gemm_nt_ref(a, b))
+    assert res["ok"], res
+    d2, _ = H.run_bf16(a, b, gpu)
+    assert np.array_equal(H.d_bits(d), H.d_bits(d2))

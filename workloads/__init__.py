@@ -23,7 +23,7 @@ class Workload:
 
     def __init__(self, name, kind, desc, **shape):
         self.name = name
-        self.kind = kind  # "dense" | "contiguous" | "masked" | "kgrouped"
+        self.kind = kind  # "dense" | "contiguous" | "masked" | "kgrouped" | "bf16"
         self.desc = desc
         self.shape = shape
 
@@ -49,6 +49,11 @@ WORKLOADS = {
         "moe_masked_16x256_n4096_k7168", "masked",
         "MoE grouped masked decode, 16 experts, max_m=256, N=4096 K=7168",
         g=16, max_m=256, n=4096, k=7168, b_std=0.02),
+    # BF16 dense GEMM on the large dense shape (operands rounded to bf16 by
+    # the caller from these fp32 draws)
+    "bf16_dense_4096x7168x16384": Workload(
+        "bf16_dense_4096x7168x16384", "bf16", "BF16 dense GEMM (M=4096 N=7168 K=16384)",
+        m=4096, n=7168, k=16384, b_std=1.0),
     # K-grouped (MoE weight-gradient shape): 4 experts' 8192 tokens each on K,
     # M and N the expert FFN's output and input widths of the MoE shapes above
     "kgrouped_4x8192_m4096_n7168": Workload(
@@ -126,7 +131,7 @@ def draw(name, seed=0):
     """Draw the named workload's inputs with its recipe."""
     w = WORKLOADS[name]
     s = w.shape
-    if w.kind == "dense":
+    if w.kind in ("dense", "bf16"):
         return draw_dense(s["m"], s["n"], s["k"], seed, s["b_std"])
     if w.kind == "contiguous":
         return draw_contiguous(s["group_rows"], s["n"], s["k"], seed, s["b_std"])
@@ -163,6 +168,10 @@ def algorithmic_work(kind, **p):
         rows = int(cnt.sum())
         experts = int((cnt > 0).sum())
         index_bytes = 4 * cnt.size
+    elif kind == "bf16":
+        # two bytes per element of A, B and D; no scales
+        m = p["m"]
+        return 2.0 * m * n * k, 2 * (m * k + n * k + m * n)
     elif kind == "kgrouped":
         # every group reads its own K columns of A and B once and writes a
         # full M x N result (zeros for an empty group)
@@ -190,6 +199,8 @@ def workload_work(name, inputs=None):
     if w.kind == "contiguous":
         mi = inputs["m_indices"] if inputs is not None else contiguous_indices(s["group_rows"])
         return algorithmic_work("contiguous", m_indices=mi, g=len(s["group_rows"]), n=s["n"], k=s["k"])
+    if w.kind == "bf16":
+        return algorithmic_work("bf16", m=s["m"], n=s["n"], k=s["k"])
     if w.kind == "kgrouped":
         return algorithmic_work("kgrouped", k_sizes=s["k_sizes"], m=s["m"], n=s["n"], k=int(sum(s["k_sizes"])))
     mm = inputs["masked_m"] if inputs is not None else np.random.default_rng(0).integers(0, s["max_m"] + 1, s["g"])
