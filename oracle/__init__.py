@@ -26,7 +26,7 @@ Modules
 e4m3   exact 256-entry decode table, round-to-nearest-even saturating encoder
 quant  1x128 (activation) and 128x128 (weight) quantisers
 gemm   dense, contiguous-grouped, masked-grouped and K-grouped reference GEMMs in fp64,
-       and the BF16 NT GEMM
+       and the BF16 NT GEMM; FC1 + SwiGLU on the masked layout
 check  the element-wise acceptance rule
 """
 
@@ -41,5 +41,8 @@ from .gemm import (  # noqa: F401
     k_grouped_ref_at,
     bf16_gemm_nt_ref,
     bf16_to_f64,
+    masked_swiglu_quant_ref,
+    masked_swiglu_ref,
+    silu,
 )
 from .check import tolerance_check, bf16_bits_to_float, bf16_round  # noqa: F401

@@ -256,3 +256,52 @@ def bf16_gemm_nt_ref(a_bits, b_bits):
     if a.shape[1] != b.shape[1]:
         raise ValueError("A and B must share K")
     return a @ b.T
+
+
+def silu(x):
+    """SiLU (swish), x * sigmoid(x), in fp64 (exp overflows to inf for
+    x < -709, where x / inf = -0 is the correctly rounded value)."""
+    x = np.asarray(x, np.float64)
+    with np.errstate(over="ignore"):
+        return x / (1.0 + np.exp(-x))
+
+
+def masked_swiglu_ref(qa, sfa, qb, sfb, masked_m):
+    """FC1 of an MoE expert on the masked layout followed by SwiGLU, in fp64.
+
+    The single-GPU slice of the fused MoE path ("Unveiling DeepGEMM" press
+    article, yeyulingfeng.com, Mega MoE section: dispatch, the first GEMM,
+    the SwiGLU activation and the second GEMM fused into one kernel).  Reading:
+    B holds each expert's FC1 weight as [gate; up], 2I rows (I gate rows,
+    then I up rows), and h = silu(A . gate^T) * (A . up^T).  Returns
+    (h, valid): h is G x max_m x I with NaN in rows past masked_m[g]."""
+    r, valid = grouped_masked_ref(qa, sfa, qb, sfb, masked_m)
+    i = qb.shape[1] // 2
+    if qb.shape[1] != 2 * i:
+        raise ValueError("B must hold gate and up halves of equal size")
+    return silu(r[..., :i]) * r[..., i:], valid
+
+
+def masked_swiglu_quant_ref(qa, sfa, qb, sfb, masked_m):
+    """FC1 + SwiGLU with h requantised as the second GEMM's A operand.
+
+    Reading: the fused MoE path hands h to the second GEMM as FP8, so h is
+    quantised with the activation rule (one fp32 scale per row and 128-wide
+    slab of I; the scaling item of the DeepGEMM pages' technical features),
+    exactly as quantize_a_1x128 does: the decision is taken in fp32 on
+    fp32(h).  Returns (hq, hs, valid): hq is G x max_m x I e4m3 codes, hs is
+    G x max_m x (I/128) fp32; rows past masked_m[g] hold code 0 and scale NaN.
+    """
+    from .quant import quantize_a_1x128
+
+    h, valid = masked_swiglu_ref(qa, sfa, qb, sfb, masked_m)
+    g, max_m, i = h.shape
+    if i % 128 != 0:
+        raise ValueError("I must be a multiple of 128")
+    hq = np.zeros((g, max_m, i), np.uint8)
+    hs = np.full((g, max_m, i // 128), np.nan, np.float32)
+    for e in range(g):
+        rows = int(valid[e].sum())
+        if rows:
+            hq[e, :rows], hs[e, :rows] = quantize_a_1x128(h[e, :rows].astype(np.float32))
+    return hq, hs, valid

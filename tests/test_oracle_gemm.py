@@ -13,7 +13,12 @@
   its groups summing to the dense result, unit scales giving a plain matmul
   per K slice, an empty group giving zero, and bad group sizes rejected;
 * the BF16 GEMM: its bf16 decode against torch's, exact-rational brute force,
-  and closed forms (ones give K, a one-hot row selects a column of B).
+  and closed forms (ones give K, a one-hot row selects a column of B);
+* SiLU against torch's and the identity silu(x) - silu(-x) = x; FC1 + SwiGLU
+  with the up half fixed to give exactly 1 (then h = silu(gate)), and with
+  the gate half fixed to give exactly 0 (then h = 0); the requantised h
+  dequantises to within half an e4m3 step of h, each block's largest |h|
+  lands on +-448, and rows past the count stay empty.
 """
 
 from fractions import Fraction
@@ -24,8 +29,9 @@ import torch
 
 from oracle import (gemm_nt_ref, gemm_nt_ref_at, grouped_contiguous_ref,
                     grouped_masked_ref, k_grouped_ref, k_grouped_ref_at, tolerance_check,
-                    bf16_gemm_nt_ref, bf16_to_f64)
+                    bf16_gemm_nt_ref, bf16_to_f64, masked_swiglu_ref, masked_swiglu_quant_ref, silu)
 from oracle.gemm import grouped_contiguous_ref_at, grouped_masked_ref_at
+from oracle.e4m3 import decode_table
 
 SPECIAL = np.array([0x7E, 0xFE, 0x01, 0x81, 0x00, 0x80, 0x07, 0x08, 0x38, 0x5F], dtype=np.uint8)
 
@@ -334,3 +340,80 @@ def test_bf16_gemm_closed_forms():
     a = np.zeros((1, k), np.uint16)
     a[0, 17] = 0x3F80
     assert np.array_equal(bf16_gemm_nt_ref(a, b)[0], bf16_to_f64(b[:, 17]))
+
+
+
+# ---- FC1 + SwiGLU (masked layout)
+
+def test_silu_against_library_and_identity():
+    x = np.linspace(-30, 30, 2001)
+    ref = torch.nn.functional.silu(torch.from_numpy(x)).numpy()
+    assert np.allclose(silu(x), ref, rtol=1e-15, atol=1e-300)
+    assert np.allclose(silu(x) - silu(-x), x, rtol=1e-15, atol=1e-15)
+    assert silu(0.0) == 0.0
+
+
+def _swiglu_case(up_code, gate_code=None, seed=41):
+    rng = np.random.default_rng(seed)
+    g, max_m, i, k = 2, 5, 128, 256
+    qa = random_codes(rng, (g, max_m, k))
+    sa = random_scales(rng, (g, max_m, k // 128))
+    qb = random_codes(rng, (g, 2 * i, k))
+    sb = random_scales(rng, (g, 2, k // 128))
+    if gate_code is not None:
+        qb[:, :i, :] = gate_code
+    # up half: A row . up row must be a known constant: put the code only at
+    # K position 0 of every up row and make every A row's K position 0 give
+    # one, with unit scales on slab 0 and zero codes elsewhere in the up rows
+    qb[:, i:, :] = 0x00
+    qb[:, i:, 0] = up_code
+    qa[:, :, 0] = 0x38  # 1.0
+    sa[:, :, 0] = 1.0
+    sb[:, 1, 0] = 1.0
+    masked_m = np.array([3, 5], np.int32)
+    return qa, sa, qb, sb, masked_m, i
+
+
+def test_swiglu_with_unit_up_is_silu_of_gate():
+    qa, sa, qb, sb, mm, i = _swiglu_case(up_code=0x38)  # up = 1.0 exactly
+    h, valid = masked_swiglu_ref(qa, sa, qb, sb, mm)
+    r, _ = grouped_masked_ref(qa, sa, qb, sb, mm)
+    gate = r[..., :i]
+    ref = torch.nn.functional.silu(torch.from_numpy(np.nan_to_num(gate))).numpy()
+    assert np.allclose(h[valid], ref[valid], rtol=1e-14, atol=0)
+    assert np.all(np.isnan(h[~valid]))
+    assert h.shape == (2, 5, i)
+
+
+def test_swiglu_with_zero_gate_is_zero():
+    qa, sa, qb, sb, mm, i = _swiglu_case(up_code=0x48, gate_code=0x00)  # gate = 0, up = 4
+    h, valid = masked_swiglu_ref(qa, sa, qb, sb, mm)
+    assert np.all(h[valid] == 0.0)
+
+
+def test_swiglu_requantised_bounds():
+    rng = np.random.default_rng(43)
+    g, max_m, i, k = 3, 40, 256, 384
+    qa = random_codes(rng, (g, max_m, k))
+    sa = random_scales(rng, (g, max_m, k // 128))
+    qb = random_codes(rng, (g, 2 * i, k))
+    sb = random_scales(rng, (g, 4, k // 128))
+    mm = np.array([40, 0, 17], np.int32)
+    hq, hs, valid = masked_swiglu_quant_ref(qa, sa, qb, sb, mm)
+    h, _ = masked_swiglu_ref(qa, sa, qb, sb, mm)
+    assert hq.shape == (g, max_m, i) and hs.shape == (g, max_m, i // 128)
+    assert np.all(hq[~valid] == 0) and np.all(np.isnan(hs[~valid]))
+    vals = decode_table()[hq].astype(np.float64)
+    hv = h[valid].reshape(-1, i // 128, 128)
+    qv = vals[valid].reshape(-1, i // 128, 128)
+    sv = hs[valid].astype(np.float64)
+    deq = qv * sv[..., None]
+    # e4m3: 3 mantissa bits (half step 2^-4 relative), subnormal step 2^-9
+    bound = np.maximum(np.abs(hv) * 2.0 ** -4, sv[..., None] * 2.0 ** -10) * (1 + 2.0 ** -20)
+    assert np.all(np.abs(deq - hv) <= bound)
+    # the largest |h| of a block maps onto the saturation value
+    top = np.take_along_axis(np.abs(qv), np.argmax(np.abs(hv), axis=-1)[..., None], -1)
+    assert np.all(top == 448.0)
+    # and the scale is that element's magnitude over 448
+    amax = np.max(np.abs(hv), axis=-1)
+    assert np.allclose(sv, amax / 448.0, rtol=2.0 ** -22)

@@ -41,6 +41,11 @@ MUTATIONS = [
     ("gemm.py", "starts = ends - sizes", "starts = ends - sizes + SLAB * (sizes > 0)"),
     ("gemm.py", "np.asarray(sfa)[:, s0:s1], qb[:, cols]", "np.asarray(sfa)[:, 0:s1 - s0], qb[:, cols]"),
     ("gemm.py", "if np.any(sizes < 0) or np.any(sizes % SLAB):", "if np.any(sizes < 0):"),
+    # SwiGLU: gate and up swapped, sigmoid of the wrong sign
+    ("gemm.py", "return silu(r[..., :i]) * r[..., i:], valid", "return silu(r[..., i:]) * r[..., :i], valid"),
+    ("gemm.py", "return x / (1.0 + np.exp(-x))", "return x / (1.0 + np.exp(x))"),
+    ("gemm.py", "hq[e, :rows], hs[e, :rows] = quantize_a_1x128(h[e, :rows].astype(np.float32))",
+     "hq[e, :rows], hs[e, :rows] = quantize_a_1x128(np.abs(h[e, :rows]).astype(np.float32))"),
     # BF16: wrong half of the fp32 word, transposed operand
     ("gemm.py", "b = np.asarray(bits, np.uint16).astype(np.uint32) << 16", "b = np.asarray(bits, np.uint16).astype(np.uint32) << 15"),
     ("gemm.py", "    return a @ b.T\n", "    return a @ b[::-1].T\n"),
