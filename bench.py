@@ -202,6 +202,29 @@ def setup_workload(torch, np, dg, W, name, dev):
             dg.k_grouped_fp8_gemm_nt((st["qa"], st["sfa"]), (st["qb"], st["sfb"]), st["d"], st["ks"])
 
         return w.kind, dict(k_sizes=inp["k_sizes"], m=m, n=n, k=k), rot, launch, None, inp
+    if w.kind == "swiglu":
+        g, max_m, inter, k = s["g"], s["max_m"], s["inter"], s["k"]
+        mm = torch.from_numpy(inp["masked_m"]).to(dev)
+        qa, sfa = dg.quantize_a_1x128(torch.from_numpy(inp["a"]).to(dev))
+        qb, sfb = dg.quantize_b_128x128(torch.from_numpy(inp["b"]).to(dev))
+        ld = dg.get_sfa_ld(max_m)
+
+        def make(i):
+            hq = torch.empty((g, max_m, inter), dtype=torch.float8_e4m3fn, device=dev)
+            hs = torch.empty((g, inter // 128, ld), dtype=torch.float32, device=dev)
+            if i == 0:
+                return {"qa": qa, "sfa": sfa, "qb": qb, "sfb": sfb, "hq": hq, "hs": hs, "mm": mm}
+            return {"qa": qa.clone(), "sfa": sfa.clone(), "qb": qb.clone(), "sfb": sfb.clone(), "hq": hq,
+                    "hs": hs, "mm": mm.clone()}
+
+        rot = Rotation(make, qa.numel() + qb.numel() + g * max_m * inter)
+        expected = int(np.clip(inp["masked_m"], 0, max_m).mean())
+
+        def launch(st):
+            dg.m_grouped_fp8_gemm_nt_masked_swiglu((st["qa"], st["sfa"]), (st["qb"], st["sfb"]),
+                                                   (st["hq"], st["hs"]), st["mm"], expected)
+
+        return w.kind, dict(masked_m=inp["masked_m"], max_m=max_m, n=2 * inter, k=k), rot, launch, None, inp
     g, max_m, n, k = s["g"], s["max_m"], s["n"], s["k"]
     mm = torch.from_numpy(inp["masked_m"]).to(dev)
     qa, sfa = dg.quantize_a_1x128(torch.from_numpy(inp["a"]).to(dev))

@@ -12,6 +12,7 @@ Layouts (all row-major, packed):
   b    [n, k] e4m3; grouped: [g, n, k]
   sfb  fp32 [ceil(n/128), k/128]; grouped: [g, ceil(n/128), k/128]
   d    bf16 [m, n]; masked: [g, max_m, n]
+  hq   (SwiGLU) e4m3 [g, max_m, inter]; hs fp32 [g, inter/128, get_sfa_ld(max_m)]
 """
 
 import ctypes
@@ -24,7 +25,7 @@ LIB_PATH = os.path.join(_PKG_DIR, "libdg.so")
 
 __all__ = [
     "DGError", "lib", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous",
-    "m_grouped_fp8_gemm_nt_masked", "quantize_a_1x128", "quantize_b_128x128",
+    "m_grouped_fp8_gemm_nt_masked", "m_grouped_fp8_gemm_nt_masked_swiglu", "quantize_a_1x128", "quantize_b_128x128",
     "k_grouped_fp8_gemm_nt", "bf16_gemm_nt", "get_m_alignment_for_contiguous_layout", "get_sfa_ld", "empty_sfa",
     "profile_next_launch",
     "reserve_workspace",
@@ -45,6 +46,7 @@ _SIGNATURES = {
     "dg_fp8_gemm_nt": [_vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _vp],
     "dg_m_grouped_fp8_gemm_nt_contiguous": [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _vp],
     "dg_m_grouped_fp8_gemm_nt_masked": [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _vp],
+    "dg_m_grouped_fp8_gemm_nt_masked_swiglu": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _vp],
     "dg_k_grouped_fp8_gemm_nt": [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _vp],
     "dg_bf16_gemm_nt": [_vp, _vp, _vp, _ci, _ci, _ci, _vp],
     "dg_get_m_alignment_for_contiguous_layout": [],
@@ -197,6 +199,36 @@ def m_grouped_fp8_gemm_nt_masked(a_pair, b_pair, d, masked_m, expected_m=0):
         _ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(d), _ptr(masked_m), g, max_m, n, k,
         int(expected_m), _stream()))
     return d
+
+
+def m_grouped_fp8_gemm_nt_masked_swiglu(a_pair, b_pair, h_pair, masked_m, expected_m=0):
+    """MoE FC1 + SwiGLU on the masked layout: B is [g, 2*inter, k] holding
+    each expert's gate rows, then its up rows; h = silu(gate) * up of the
+    valid rows is written as e4m3 codes hq [g, max_m, inter] with 1x128 fp32
+    scales hs [g, inter/128, get_sfa_ld(max_m)], the A operand layout of the
+    masked GEMM."""
+    a, sfa = a_pair
+    b, sfb = b_pair
+    hq, hs = h_pair
+    _need(a, "a", _FP8, 3)
+    _need(b, "b", _FP8, 3)
+    _need(hq, "hq", _FP8, 3)
+    _need(sfa, "sfa", (torch.float32,), 3)
+    _need(sfb, "sfb", (torch.float32,), 3)
+    _need(hs, "hs", (torch.float32,), 3)
+    _need(masked_m, "masked_m", (torch.int32,), 1)
+    g, max_m, k = a.shape
+    inter = b.shape[1] // 2
+    if b.shape[0] != g or b.shape[2] != k or b.shape[1] != 2 * inter or masked_m.numel() != g:
+        raise ValueError("shape mismatch")
+    if tuple(hq.shape) != (g, max_m, inter) or tuple(hs.shape) != (g, inter // 128, get_sfa_ld(max_m)):
+        raise ValueError("output shape mismatch")
+    if tuple(sfa.shape) != (g, k // 128, get_sfa_ld(max_m)) or tuple(sfb.shape) != (g, (2 * inter + 127) // 128, k // 128):
+        raise ValueError("scale shape mismatch")
+    _check(lib().dg_m_grouped_fp8_gemm_nt_masked_swiglu(
+        _ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(hq), _ptr(hs), _ptr(masked_m), g, max_m, inter, k,
+        int(expected_m), _stream()))
+    return hq, hs
 
 
 def k_grouped_fp8_gemm_nt(a_pair, b_pair, d, k_sizes):

@@ -89,16 +89,17 @@ int current_device(int* dev, DeviceInfo** info) {
 // ---- tile configurations (compile-time instantiations; the host picks one)
 struct Config {
   const char* name;
-  int variant, bm, bn, wm, wn, nst, sched, dtype;
+  int variant, bm, bn, wm, wn, nst, sched, dtype, epi;
   const void* fn;
   int smem;
   int threads() const { return wm * wn * 64; }
 };
 
-template <int BM, int BN, int WM, int WN, int NST, int VAR, int SCHED = dg::kInterleaved, int DT = dg::kFp8>
+template <int BM, int BN, int WM, int WN, int NST, int VAR, int SCHED = dg::kInterleaved, int DT = dg::kFp8,
+          int EPI = dg::kEpiBf16>
 Config make_config(const char* name) {
-  return Config{name, VAR, BM, BN, WM, WN, NST, SCHED, DT,
-                reinterpret_cast<const void*>(&dg::gemm_fp8_nt_kernel<BM, BN, WM, WN, NST, VAR, SCHED, DT>),
+  return Config{name, VAR, BM, BN, WM, WN, NST, SCHED, DT, EPI,
+                reinterpret_cast<const void*>(&dg::gemm_fp8_nt_kernel<BM, BN, WM, WN, NST, VAR, SCHED, DT, EPI>),
                 dg::Smem<BM, BN, NST>::kBytes};
 }
 
@@ -142,22 +143,29 @@ const Config* configs(int* count) {
       make_config<256, 256, 2, 4, 2, dg::kDense, dg::kInterleaved, dg::kBf16>("bf16_256x256_w8_s2"),
       make_config<128, 128, 2, 2, 2, dg::kDense, dg::kInterleaved, dg::kBf16>("bf16_128x128_w4_s2"),
       make_config<64, 32, 2, 2, 4, dg::kDense, dg::kInterleaved, dg::kBf16>("bf16_64x32_w4_s4"),
+      // MoE FC1 + SwiGLU + FP8 requantisation, masked layout (a 256-column
+      // tile = 128 gate + 128 up columns = one 128-wide block of h)
+      make_config<256, 256, 2, 4, 2, dg::kMasked, dg::kPingPong, dg::kFp8, dg::kEpiSwigluFp8>("swiglu_256x256_w8_s2_pp"),
+      make_config<256, 256, 2, 4, 2, dg::kMasked, dg::kInterleaved, dg::kFp8, dg::kEpiSwigluFp8>("swiglu_256x256_w8_s2"),
+      make_config<128, 256, 2, 4, 3, dg::kMasked, dg::kInterleaved, dg::kFp8, dg::kEpiSwigluFp8>("swiglu_128x256_w8_s3"),
+      make_config<64, 256, 1, 4, 3, dg::kMasked, dg::kInterleaved, dg::kFp8, dg::kEpiSwigluFp8>("swiglu_64x256_w4_s3"),
   };
   *count = sizeof(table) / sizeof(table[0]);
   return table;
 }
 
-const Config* find_config(const char* name, int variant, int dtype = dg::kFp8) {
+const Config* find_config(const char* name, int variant, int dtype = dg::kFp8, int epi = dg::kEpiBf16) {
   int cnt = 0;
   const Config* t = configs(&cnt);
   for (int i = 0; i < cnt; ++i)
-    if (t[i].variant == variant && t[i].dtype == dtype && strcmp(t[i].name, name) == 0) return &t[i];
+    if (t[i].variant == variant && t[i].dtype == dtype && t[i].epi == epi && strcmp(t[i].name, name) == 0)
+      return &t[i];
   return nullptr;
 }
 
 // DG_FORCE_CONFIG=<name> pins the configuration of the variant it names (for
 // tuning sweeps); an unknown name is an error rather than silently ignored.
-int forced_config(int variant, const Config** out, int dtype = dg::kFp8) {
+int forced_config(int variant, const Config** out, int dtype = dg::kFp8, int epi = dg::kEpiBf16) {
   *out = nullptr;
   const char* e = getenv("DG_FORCE_CONFIG");
   if (!e || !*e) return DG_OK;
@@ -166,7 +174,7 @@ int forced_config(int variant, const Config** out, int dtype = dg::kFp8) {
   bool known = false;
   for (int i = 0; i < cnt; ++i) known = known || strcmp(t[i].name, e) == 0;
   if (!known) return fail(DG_ERR_INVALID_ARGUMENT, "DG_FORCE_CONFIG names no configuration: %s", e);
-  *out = find_config(e, variant, dtype);
+  *out = find_config(e, variant, dtype, epi);
   return DG_OK;
 }
 
@@ -483,6 +491,40 @@ int dg_k_grouped_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* 
   p.num_tiles = num_groups * p.tiles_m * p.tiles_n;
   p.splits = 1;
   p.split_slabs = p.kb_count;
+  return launch(*c, p, p.num_tiles, (hipStream_t)stream);
+}
+
+int dg_m_grouped_fp8_gemm_nt_masked_swiglu(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                                           uint8_t* hq, float* hs, const int32_t* masked_m, int num_groups,
+                                           int max_m, int inter, int k, int expected_m, dg_stream_t stream) {
+  if (!a || !sfa || !b || !sfb || !hq || !hs || !masked_m)
+    return fail(DG_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (num_groups < 0) return fail(DG_ERR_INVALID_ARGUMENT, "num_groups must be >= 0 (got %d)", num_groups);
+  if (max_m < 0) return fail(DG_ERR_INVALID_ARGUMENT, "max_m must be >= 0 (got %d)", max_m);
+  if (expected_m < 0) return fail(DG_ERR_INVALID_ARGUMENT, "expected_m must be >= 0 (got %d)", expected_m);
+  if (inter < 128 || inter % 128 != 0 || inter > (1 << 29))
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "inter must be a positive multiple of 128 (got %d)", inter);
+  if (int s = check_k_n(2 * inter, k)) return s;
+  if (int s = check_rows(max_m, k)) return s;
+  if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(hq) || !aligned16(hs) ||
+      (reinterpret_cast<uintptr_t>(masked_m) & 3u))
+    return fail(DG_ERR_MISALIGNED, "pointers must be 16-byte aligned (masked_m 4-byte)");
+  if (num_groups == 0 || max_m == 0) return ok();
+  int dev;
+  DeviceInfo* info;
+  if (int s = current_device(&dev, &info)) return s;
+  const Config* c;
+  if (int s = forced_config(dg::kMasked, &c, dg::kFp8, dg::kEpiSwigluFp8)) return s;
+  if (!c)
+    c = find_config(max_m <= 64 ? "swiglu_64x256_w4_s3" : "swiglu_256x256_w8_s2_pp", dg::kMasked, dg::kFp8,
+                    dg::kEpiSwigluFp8);
+  dg::GemmParams p{};
+  p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.masked_m = masked_m;
+  p.hq = hq; p.hs = hs; p.inter = inter;
+  p.num_groups = num_groups;
+  fill_common(p, *c, max_m, 2 * inter, k);
+  p.tiles_n = inter / 128;  // one tile per 128 h columns (128 gate + 128 up rows of B)
+  p.num_tiles = num_groups * p.tiles_m * p.tiles_n;
   return launch(*c, p, p.num_tiles, (hipStream_t)stream);
 }
 

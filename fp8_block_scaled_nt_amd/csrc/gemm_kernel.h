@@ -39,6 +39,8 @@
 #include <type_traits>
 #include <utility>
 
+#include "quant_kernel.h"
+
 namespace dg {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -52,6 +54,10 @@ enum Variant { kDense = 0, kContiguous = 1, kMasked = 2, kKGrouped = 3 };
 // slab row then holds 64 K values).
 enum DType { kFp8 = 0, kBf16 = 1 };
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+// Epilogue: store D as bf16, or (MoE FC1 on the masked layout) pair each
+// gate column with its up column, apply SwiGLU and quantise h with the 1 x 128
+// activation rule, so the second GEMM reads h as FP8 without a round trip.
+enum Epilogue { kEpiBf16 = 0, kEpiSwigluFp8 = 1 };
 
 constexpr int kSlab = 128;        // K bytes per slab (one scale per slab)
 constexpr int kNumXcd = 8;        // MI355X: 8 XCDs, workgroups dealt round-robin
@@ -70,6 +76,9 @@ struct GemmParams {
   const int32_t* m_indices;  // contiguous layout
   const int32_t* masked_m;   // masked layout
   const int32_t* k_sizes;    // K-grouped layout: K columns of each group
+  uint8_t* hq;               // SwiGLU epilogue: h codes [groups][m][inter]
+  float* hs;                 // SwiGLU epilogue: h scales [groups][inter/128][sfa_ld]
+  int inter;                 // SwiGLU epilogue: I (B holds 2I rows: gate, then up)
   int m;                     // rows of A (dense, contiguous) or max_m (masked)
   int n;
   int k;
@@ -235,7 +244,8 @@ __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 // groups that alternate load and compute steps, see below).
 enum Schedule { kInterleaved = 0, kPingPong = 1 };
 
-template <int BM, int BN, int WM, int WN, int NST, int VAR, int SCHED = kInterleaved, int DT = kFp8>
+template <int BM, int BN, int WM, int WN, int NST, int VAR, int SCHED = kInterleaved, int DT = kFp8,
+          int EPI = kEpiBf16>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p) {
   constexpr int kThreads = WM * WN * 64;
   constexpr int kWaves = WM * WN;
@@ -247,6 +257,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be whole fragments");
   static_assert(BM <= kThreads, "row-tag pass needs one thread per tile row");
   static_assert(NST >= 2, "pipeline shape");
+  // SwiGLU: a tile covers 128 h columns (one activation scale block), each
+  // wave TN / 2 of them: its first TN / 2 tile columns are gate rows of B and
+  // its last TN / 2 the matching up rows, so gate and up meet in one lane.
+  static_assert(EPI == kEpiBf16 || (VAR == kMasked && DT == kFp8 && BN == 256 && TN % 32 == 0),
+                "SwiGLU epilogue shape");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_flag;  // contiguous: block expert; split-K: last-arriver flag
@@ -367,6 +382,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
     const int r = 8 * j + (lane >> 3);
     const int chunk = (lane & 7) ^ swz(r);
     int row = n0 + r;
+    if constexpr (EPI == kEpiSwigluFp8) {
+      const int q = r % TN;
+      row = (q < TN / 2 ? 0 : p.inter) + tn * (BN / 2) + (r / TN) * (TN / 2) + q % (TN / 2);
+    }
     row = row < p.n ? row : p.n - 1;
     b_off[jj] = ((uint32_t)row * (uint32_t)K) | (16u * chunk);
     b_live += j < kJb ? 1 : 0;
@@ -384,11 +403,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
     sa_off = (uint32_t)row;
   }
   // B block scales of the 128-row blocks this tile touches (every wave)
+  // (SwiGLU: the gate block of the tile's h columns, then the up block)
   const int nb0 = n0 >> 7;
-  const bool sb_lane = lane < S::kSbCount;
+  const bool sb_lane = lane < (EPI == kEpiSwigluFp8 ? 2 : S::kSbCount);
   uint32_t sb_off;
   {
-    int blk = nb0 + lane;
+    int blk = EPI == kEpiSwigluFp8 ? (lane == 0 ? tn : (p.inter >> 7) + tn) : nb0 + lane;
     blk = blk < p.nb_count ? blk : p.nb_count - 1;
     sb_off = (uint32_t)blk * (uint32_t)p.kb_count;  // sfb row stride: all K slabs
   }
@@ -437,8 +457,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   // index of each fragment's B scale block among the tile's blocks
   int sb_idx[FN];
   #pragma unroll
-  for (int j = 0; j < FN; ++j) sb_idx[j] = ((n0 + wn * TN + j * 16) >> 7) - nb0;
-  constexpr bool kSbUniform = (128 % TN) == 0;  // a wave's columns lie in one block
+  for (int j = 0; j < FN; ++j)
+    sb_idx[j] = EPI == kEpiSwigluFp8 ? (j < FN / 2 ? 0 : 1) : ((n0 + wn * TN + j * 16) >> 7) - nb0;
+  // a wave's columns lie in one block
+  constexpr bool kSbUniform = EPI == kEpiBf16 && (128 % TN) == 0;
   // fragments of this wave that hold at least one valid row
   int fm_valid = FM;
   if (VAR == kMasked) {
@@ -475,7 +497,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
     // refilled.
     static_assert(BM == 256 && BN == 256 && WM == 2 && WN == 4 && NST == 2, "ping-pong tile shape");
     static_assert(DT == kFp8, "ping-pong schedule is written for fp8 operands");
-    static_assert(kSbUniform, "a wave's columns must share one B scale block");
+    static_assert(kSbUniform || EPI == kEpiSwigluFp8, "a wave's columns must share one B scale block");
     constexpr int kFh = 4;          // A fragments per chunk
     constexpr int kNch = FM / kFh;  // chunks per slab
     const int grp = wm;
@@ -487,7 +509,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
     v8i bq[FN];
     v8i aq[kFh];
     v4f sq[kFh];
-    float sbq = 0.f;
+    float sbq = 0.f;   // B scale of the wave's columns (SwiGLU: of the gate half)
+    float sbq2 = 0.f;  // SwiGLU: B scale of the up half
     // LDS reads address a per-step base register plus an immediate offset;
     // the opaque base keeps the compiler from precomputing a register per
     // fragment and stage (a stage is wider than the 16-bit offset field).
@@ -502,6 +525,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
       if (c == 0) {
         const float* sSb = (const float*)(st + S::kA + S::kB + S::kSa);
         sbq = sSb[sb_idx[0]];
+        if constexpr (EPI == kEpiSwigluFp8) sbq2 = sSb[1];
         const uint32_t bb_lo = lds_base(st + S::kA + wn * FN * 2048) + frag_lo;
         const uint32_t bb_hi = bb_lo - frag_lo + frag_hi;
 #pragma unroll
@@ -540,7 +564,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
           const int u = t - kLagPP;
           const int i = u / FN, j = u % FN;
           if (c * kFh + i < fm_valid) {
-            const v4f sc = sq[i] * sbq;
+            const v4f sc = sq[i] * ((EPI == kEpiSwigluFp8 && j >= FN / 2) ? sbq2 : sbq);
             const v4f pv = pr[u % (kLagPP + 1)];
             acc[c * kFh + i][j][0] = __builtin_fmaf(pv[0], sc[0], acc[c * kFh + i][j][0]);
             acc[c * kFh + i][j][1] = __builtin_fmaf(pv[1], sc[1], acc[c * kFh + i][j][1]);
@@ -709,6 +733,106 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   }
 
   wait_vmem_all();  // no LDS DMA may be in flight past this point
+
+  if constexpr (EPI == kEpiSwigluFp8) {
+    // ---- SwiGLU epilogue: h = silu(gate) * up in fp32 from the
+    // accumulators, then h's 1 x 128 activation quantisation.  The tile holds
+    // all 128 h columns of its block, so a row's amax is a max over the 16
+    // lanes of a fragment row, the wave's fragments and the WN waves of a
+    // tile row (through LDS).  One thread per tile row then forms the row's
+    // scale and its reciprocal, and the waves quantise their h values with
+    // them.  Codes are staged in LDS and leave as 16-byte row stores; scales
+    // go to the slab-major layout the masked GEMM reads its A scales from.
+    // Rows past the expert's count are not written.
+    constexpr int FH = FN / 2;
+    constexpr int kHalf = TN / 2;             // h columns per wave
+    constexpr int kCodePitch = BN / 2 + 16;   // bytes per staged code row
+    static_assert(WN * BM * 4 + 2 * BM * 4 + BM * kCodePitch <= S::kBytes, "SwiGLU staging fits the LDS");
+    static_assert(BM <= kThreads, "one thread per tile row forms the scales");
+    block_barrier();  // every wave is done reading the last stage
+    float* s_amax = (float*)smem;                 // [WN][BM] per-wave row amax
+    float* s_sc = s_amax + WN * BM;               // [BM] row scale
+    float* s_rc = s_sc + BM;                      // [BM] its refined reciprocal
+    uint8_t* s_code = (uint8_t*)(s_rc + BM);      // [BM][kCodePitch]
+    // max over the 16 lanes of a DPP row (the lanes that hold one fragment
+    // row): quad swaps, then mirrors inside 8 and 16 lanes
+    auto row16_max = [](float v) {
+      auto dpp = [](float x, auto ctrl) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value, 0xF, 0xF, false));
+      };
+      v = fmaxf(v, dpp(v, std::integral_constant<int, 0xB1>{}));   // quad_perm [1,0,3,2]
+      v = fmaxf(v, dpp(v, std::integral_constant<int, 0x4E>{}));   // quad_perm [2,3,0,1]
+      v = fmaxf(v, dpp(v, std::integral_constant<int, 0x141>{}));  // row_half_mirror
+      v = fmaxf(v, dpp(v, std::integral_constant<int, 0x140>{}));  // row_mirror
+      return v;
+    };
+    #pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      if (i >= fm_valid) continue;
+      #pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float mx = 0.f;
+        #pragma unroll
+        for (int jh = 0; jh < FH; ++jh) {
+          // silu(g) = g / (1 + exp(-g)), the quotient through v_rcp_f32 (1 ulp);
+          // exp(-g) = inf for g < -88 gives -0, the rounded value of silu there
+          const float gt = acc[i][jh][e];
+          const float h = gt * __builtin_amdgcn_rcpf(1.f + __expf(-gt)) * acc[i][jh + FH][e];
+          acc[i][jh][e] = h;
+          mx = fmaxf(mx, fabsf(h));
+        }
+        mx = row16_max(mx);
+        if ((lane & 15) == 0) s_amax[wn * BM + wm * TM + i * 16 + 4 * (lane >> 4) + e] = mx;
+      }
+    }
+    block_barrier();
+    if (threadIdx.x < BM) {
+      const int rl = threadIdx.x;
+      float amax = s_amax[rl];
+      #pragma unroll
+      for (int w = 1; w < WN; ++w) amax = fmaxf(amax, s_amax[w * BM + rl]);
+      amax = fmaxf(amax, kAmaxFloor);
+      const float sc = amax / kE4m3Max;  // correctly rounded (build flag)
+      // reciprocal refined by one Newton step (for the quotients below)
+      float y = __builtin_amdgcn_rcpf(sc);
+      y = __builtin_fmaf(__builtin_fmaf(-sc, y, 1.f), y, y);
+      s_sc[rl] = sc;
+      s_rc[rl] = y;
+      if (m0 + rl < valid_rows) p.hs[((size_t)g * (p.inter >> 7) + tn) * p.sfa_ld + m0 + rl] = sc;
+    }
+    block_barrier();
+    #pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      if (i >= fm_valid) continue;
+      const int r0 = wm * TM + i * 16 + 4 * (lane >> 4);  // the lane's 4 rows: r0 .. r0 + 3
+      const v4f sc4 = *(const v4f*)(s_sc + r0);
+      const v4f y4 = *(const v4f*)(s_rc + r0);
+      #pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // h / sc by Markstein's method: the quotient through the refined
+        // reciprocal, corrected once by its exact residual (correctly rounded
+        // whenever the refined reciprocal is; sc lies in [2^-23, 2^120], so
+        // nothing over- or underflows)
+        #pragma unroll
+        for (int jh = 0; jh < FH; ++jh) {
+          const float hv = acc[i][jh][e];
+          const float q0 = hv * y4[e];
+          const float q = __builtin_fmaf(__builtin_fmaf(-q0, sc4[e], hv), y4[e], q0);
+          s_code[(r0 + e) * kCodePitch + wn * kHalf + jh * 16 + (lane & 15)] = e4m3_code(q);
+        }
+      }
+    }
+    block_barrier();
+    const int rows_here = min(BM, valid_rows - m0);
+    constexpr int kChunks = BN / 2 / 16;  // 16-byte chunks per h row of the tile
+    uint8_t* HQ = p.hq + (size_t)g * p.m * p.inter + (size_t)tn * (BN / 2);
+    for (int idx = threadIdx.x; idx < BM * kChunks; idx += kThreads) {
+      const int rl = idx / kChunks, ch = idx % kChunks;
+      if (rl >= rows_here) break;
+      *(v4i*)(HQ + (size_t)(m0 + rl) * p.inter + ch * 16) = *(const v4i*)(s_code + rl * kCodePitch + ch * 16);
+    }
+    return;
+  }
 
   // ---- split-K fix-up: publish this split's partial tile; the last split
   // to arrive adds all partials in split order (deterministic) and goes on to

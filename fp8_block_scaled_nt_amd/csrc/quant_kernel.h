@@ -32,6 +32,12 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
   return (uint32_t)w;
 }
 
+// One e4m3 code (the low byte of a packed conversion), saturated at +-448.
+__device__ __forceinline__ uint8_t e4m3_code(float x) {
+  x = fminf(fmaxf(x, -kE4m3Max), kE4m3Max);
+  return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false) & 0xFF);
+}
+
 // A quantiser: one wave covers two slabs of one row; lane l holds 4
 // consecutive floats of slab (l / 32).  Rows in [m, ld) get a zero scale.
 __global__ __launch_bounds__(256) void quant_a_kernel(const float* __restrict__ x, uint8_t* __restrict__ q,

@@ -111,6 +111,39 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const ui
                                     dg_stream_t stream);
 
 /*
+ * MoE FC1 + SwiGLU on the masked layout, with h requantised for the second
+ * GEMM: the single-GPU slice of the fused MoE kernel the pages describe
+ * (the popular-press article on DeepGEMM, yeyulingfeng.com, section 04 on
+ * Mega MoE: dispatch, the first GEMM, the SwiGLU activation, the second GEMM
+ * and combine in one kernel; dispatch and combine across GPUs are not part of
+ * this call).
+ * B holds each expert's FC1 weight as [gate; up]: rows 0..inter-1 are the
+ * gate projection, rows inter..2*inter-1 the up projection.  For expert g
+ * and valid row m (m < clamp(masked_m[g], 0, max_m)):
+ *
+ *   gate[j] = FP8 GEMM of A[g][m] with B[g][j]           (as dg_m_grouped_fp8_gemm_nt_masked,
+ *   up[j]   = FP8 GEMM of A[g][m] with B[g][inter + j]    but kept in fp32)
+ *   h[j]    = silu(gate[j]) * up[j],   silu(x) = x / (1 + exp(-x))
+ *
+ * and h is quantised with the activation rule of dg_quantize_a_1x128 (per
+ * row and 128-wide block of h: amax floored at 1e-4, s = amax / 448,
+ * code = e4m3(h / s)), all in fp32.  Layouts:
+ *     A   [num_groups][max_m][k] e4m3, sfa [num_groups][k/128][dg_get_sfa_ld(max_m)]
+ *     B   [num_groups][2*inter][k] e4m3, sfb [num_groups][2*inter/128][k/128]
+ *     hq  [num_groups][max_m][inter] e4m3 codes (output)
+ *     hs  [num_groups][inter/128][dg_get_sfa_ld(max_m)] fp32 scales (output)
+ * hq and hs are exactly the A operand of a masked GEMM with k = inter, so
+ * the second layer reads them without a conversion pass.  inter must be a
+ * positive multiple of 128 and k of 128; pointers 16-byte aligned
+ * (masked_m 4-byte).  Rows past an expert's count, and the padding entries
+ * of hs, are left untouched.  expected_m is a hint as for the masked GEMM.
+ * Errors as for the other entry points; nothing is allocated.
+ */
+int dg_m_grouped_fp8_gemm_nt_masked_swiglu(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                                           uint8_t* hq, float* hs, const int32_t* masked_m, int num_groups,
+                                           int max_m, int inter, int k, int expected_m, dg_stream_t stream);
+
+/*
  * BF16 NT GEMM: D[m][n] = bf16( sum_k A[m, k] * B[n, k] ) for bf16 A [m][k]
  * and B [n][k] (bit patterns in uint16), fp32 accumulation, no scales
  * ("DeepGEMM: making LLM matrix multiplication fly", pomoai.com, core

@@ -269,9 +269,9 @@ def silu(x):
 def masked_swiglu_ref(qa, sfa, qb, sfb, masked_m):
     """FC1 of an MoE expert on the masked layout followed by SwiGLU, in fp64.
 
-    The single-GPU slice of the fused MoE path ("Unveiling DeepGEMM" press
-    article, yeyulingfeng.com, Mega MoE section: dispatch, the first GEMM,
-    the SwiGLU activation and the second GEMM fused into one kernel).  Reading:
+    The single-GPU slice of the fused MoE path (the popular-press article on
+    DeepGEMM, yeyulingfeng.com, section 04 on Mega MoE: dispatch, the first
+    GEMM, the SwiGLU activation and the second GEMM fused into one kernel).  Reading:
     B holds each expert's FC1 weight as [gate; up], 2I rows (I gate rows,
     then I up rows), and h = silu(A . gate^T) * (A . up^T).  Returns
     (h, valid): h is G x max_m x I with NaN in rows past masked_m[g]."""

@@ -124,6 +124,40 @@ def run_bf16(a_bits, b_bits, dev, guard=256):
     return d, flat
 
 
+SENTINEL_CODE = 0x7F            # e4m3 NaN: never produced (codes saturate at 448)
+SENTINEL_SCALE = 0x7FC0BEEF     # a NaN bit pattern for untouched fp32 scales
+
+
+def run_swiglu(qa, sa, qb, sb, masked_m, dev, expected_m=0, guard=256):
+    """Fused FC1 + SwiGLU + requantisation.  Returns (hq, hs, hq_flat,
+    hs_flat): hq as uint8 [g][max_m][inter], hs as raw uint32 bits in the
+    device layout [g][inter/128][ld], and the whole prefilled buffers."""
+    g, max_m, k = qa.shape
+    inter = qb.shape[1] // 2
+    ld = sfa_ld(max_m)
+    a = codes_to_device(qa, dev)
+    b = codes_to_device(qb, dev)
+    sfa = f32_to_device(np.stack([slab_major(sa[i]) for i in range(g)]), dev)
+    sfb = f32_to_device(sb, dev)
+    mm = torch.from_numpy(np.asarray(masked_m, np.int32)).to(dev)
+    nq = g * max_m * inter
+    ns = g * (inter // 128) * ld
+    hq_flat = torch.full((nq + guard,), SENTINEL_CODE, dtype=torch.uint8, device=dev)
+    hs_flat = torch.full((ns + guard,), SENTINEL_SCALE, dtype=torch.int32, device=dev)
+    hq = hq_flat[:nq].view(g, max_m, inter)
+    hs = hs_flat[:ns].view(torch.float32).view(g, inter // 128, ld)
+    dg.m_grouped_fp8_gemm_nt_masked_swiglu((a, sfa), (b, sfb), (hq.view(torch.float8_e4m3fn), hs), mm, expected_m)
+    torch.cuda.synchronize()
+    return (hq.cpu().numpy(), hs_flat[:ns].view(g, inter // 128, ld).cpu().numpy().view(np.uint32),
+            hq_flat, hs_flat)
+
+
+def swiglu_guards_untouched(hq_flat, hs_flat, nq, ns):
+    tq = hq_flat[nq:].cpu().numpy()
+    ts = hs_flat[ns:].cpu().numpy().view(np.uint32)
+    return bool(np.all(tq == SENTINEL_CODE) and np.all(ts == SENTINEL_SCALE))
+
+
 def guard_untouched(flat, numel):
     tail = flat[numel:].cpu().numpy()
     return bool(np.all(tail == SENTINEL))

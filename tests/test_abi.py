@@ -85,6 +85,20 @@ def test_k_grouped_validation(lib):
     assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 2, 0, 64, 256, None) == 0       # m = 0: no-op
 
 
+def test_swiglu_validation(lib):
+    f = lib.dg_m_grouped_fp8_gemm_nt_masked_swiglu
+    #       a     sfa   b     sfb   hq    hs    masked_m   g  max_m inter  k  expected_m
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD, 4, 64, 256, 256, 0, None) == 1   # null hs
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 4, -1, 256, 256, 0, None) == 1   # negative max_m
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 4, 64, 192, 256, 0, None) == 2   # inter not whole blocks
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 4, 64, 0, 256, 0, None) == 2
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 4, 64, 256, 200, 0, None) == 2   # k not whole slabs
+    assert f(GOOD, GOOD, GOOD, GOOD, ODD, GOOD, GOOD, 4, 64, 256, 256, 0, None) == 3    # misaligned hq
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, P(0x10002), 4, 64, 256, 256, 0, None) == 3
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 0, 64, 256, 256, 0, None) == 0   # no groups: no-op
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 4, 0, 256, 256, 0, None) == 0    # max_m = 0: no-op
+
+
 def test_bf16_validation(lib):
     f = lib.dg_bf16_gemm_nt
     assert f(None, GOOD, GOOD, 64, 64, 128, None) == 1      # null a

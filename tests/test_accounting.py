@@ -37,6 +37,10 @@ def test_named_workload_sizes():
     assert b == 628256768
     f, b = W.workload_work("moe_masked_16x256_n4096_k7168")
     assert b == 502088928 and f == 2.0 * 2067 * 4096 * 7168
+    # the fused FC1 + SwiGLU on the same inputs: D (2 bytes x 4096) becomes h
+    # codes (1 byte x 2048) plus one fp32 scale per 128 of them
+    f2, b2 = W.workload_work("moe_swiglu_16x256_i2048_k7168")
+    assert f2 == f and b2 == b - 2067 * 4096 * 2 + 2067 * 2048 + 2067 * 16 * 4
 
 
 def test_masked_draw_recipe():

@@ -1,0 +1,329 @@
+"""GPU parity of the fused MoE FC1 + SwiGLU + FP8 requantisation on the
+masked layout against the oracle (oracle.masked_swiglu_ref and
+oracle.masked_swiglu_quant_ref).
+
+The kernel takes each h code in fp32 from its fp32 accumulators; the oracle
+takes it on fp32(exact h); both apply the same rule (scale = amax / 448,
+code = e4m3(h / scale)).  So the checks are intervals around the exact h:
+
+* tol bounds |kernel h - exact h| per element;
+* a row block's scale must lie in [fp32(max(amax - tol) / 448),
+  fp32(max(amax + tol) / 448)] (amax floored at 1e-4);
+* with the kernel's scale s, a code is fixed wherever (h - tol) / s and
+  (h + tol) / s encode to the same code: there the codes must be equal, and
+  elsewhere the kernel's code must lie between the two.
+
+Two input families set tol:
+
+* exact-arithmetic inputs: e4m3 codes whose exponents lie in [-1, 1] and
+  power-of-two scales.  Inside an MFMA group of 8 products the exponent sums
+  then span at most 4, so the group truncation (the measured in-slab model:
+  products cut to 2^(E - 13)) loses nothing, and every slab sum, promotion and
+  running sum is exact in fp32 (the test checks that on the CPU).  The
+  accumulators are then the exact gate and up, and tol only covers the fp32
+  SiLU and product (2^-17 |h|): almost every code is fixed, and must match.
+* workload-like inputs (N(0,1) activations, N(0, 0.02^2) weights, the
+  masked workload's recipe): tol is the GEMM acceptance rule on gate and up
+  (8e-3 |x| + 1e-3 rms) carried through h = silu(g) u.  That rule is loose
+  next to the e4m3 grid (it leaves ~80% of the codes open), so these tests
+  also require that at least 98% of the codes equal the oracle's: an
+  empirical floor (the kernel's accumulators sit ~1e-4 relative from the
+  exact values, which moves a code only when h / s is that close to a
+  rounding boundary, well under 1% of codes).
+
+Rows past an expert's count keep their sentinels (codes 0x7F, a NaN scale
+pattern), as do the scale layout's padding entries and the guard bands.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from oracle.e4m3 import decode_table, encode
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+T = decode_table()
+SILU_DERIV_MAX = 1.0999  # max over x of |d/dx x sigmoid(x)|
+CONFIGS = ["swiglu_256x256_w8_s2_pp", "swiglu_256x256_w8_s2", "swiglu_128x256_w8_s3", "swiglu_64x256_w4_s3"]
+
+
+def exact_case(g, max_m, inter, k, masked_m, seed):
+    """Codes with exponent fields 6..8 (|v| in [0.5, 3.75]), random signs and
+    mantissas; power-of-two scales, different per B block."""
+    rng = np.random.default_rng(seed)
+
+    def codes(*shape):
+        e = rng.integers(6, 9, shape)
+        m = rng.integers(0, 8, shape)
+        sgn = rng.integers(0, 2, shape)
+        return ((sgn << 7) | (e << 3) | m).astype(np.uint8)
+
+    qa = codes(g, max_m, k)
+    qb = codes(g, 2 * inter, k)
+    sa = np.exp2(rng.integers(-5, -2, (g, max_m, k // 128))).astype(np.float32)
+    sb = np.exp2(rng.integers(-3, 0, (g, 2 * inter // 128, k // 128))).astype(np.float32)
+    return qa, sa, qb, sb, np.asarray(masked_m, np.int32)
+
+
+def assert_fp32_exact(qa, sa, qb, sb):
+    """Every slab sum, promoted term and running sum of every output is an
+    fp32 value (computed exactly in fp64: the operands are short dyadics)."""
+    g, max_m, k = qa.shape
+    n = qb.shape[1]
+    for e in range(g):
+        a = T[qa[e]].astype(np.float64)
+        b = T[qb[e]].astype(np.float64)
+        acc = np.zeros((max_m, n))
+        for kb in range(k // 128):
+            sl = slice(128 * kb, 128 * kb + 128)
+            p = a[:, sl] @ b[:, sl].T
+            assert np.array_equal(p.astype(np.float32), p)
+            term = p * sa[e, :, kb][:, None] * np.repeat(sb[e, :, kb], 128)[None, :n]
+            acc = acc + term
+            assert np.array_equal(acc.astype(np.float32), acc)
+
+
+def workload_case(g, max_m, inter, k, masked_m, seed):
+    x = W.draw_masked(g, max_m, 2 * inter, k, seed=seed, masked_m=masked_m)
+    qas = [oracle.quantize_a_1x128(x["a"][i]) for i in range(g)]
+    qbs = [oracle.quantize_b_128x128(x["b"][i]) for i in range(g)]
+    return (np.stack([q for q, _ in qas]), np.stack([s for _, s in qas]),
+            np.stack([q for q, _ in qbs]), np.stack([s for _, s in qbs]), x["masked_m"])
+
+
+def rms(x):
+    return float(np.sqrt(np.mean(np.square(x)))) if x.size else 0.0
+
+
+def rule_tol(gate, up, rms_g, rms_u):
+    """GEMM acceptance rule on gate and up (rms over the call's valid
+    outputs), carried through silu(g) * u, plus the fp32 SiLU and product."""
+    tg = oracle.check.REL_TOL * np.abs(gate) + oracle.check.ABS_TOL_RMS * rms_g
+    tu = oracle.check.REL_TOL * np.abs(up) + oracle.check.ABS_TOL_RMS * rms_u
+    # |silu(g') u' - silu(g) u| <= |silu'| max |u'| |g' - g| + |silu(g)| |u' - u|
+    return (SILU_DERIV_MAX * (np.abs(up) + tu) * tg + np.abs(oracle.silu(gate)) * tu
+            + 2.0 ** -17 * np.abs(oracle.silu(gate) * up))
+
+
+def f32(x):
+    return np.asarray(x, np.float64).astype(np.float32)
+
+
+def check_rows(hq, hs_bits, h, tol, label):
+    """hq: kernel codes [rows][I]; hs_bits: kernel scale bits [rows][I/128];
+    h, tol: exact h and its tolerance [rows][I].  Returns the number of codes
+    the intervals fix (+0 and -0 count as one value) and the number checked."""
+    rows, inter = h.shape
+    nb = inter // 128
+    s_k = hs_bits.view(np.float32).astype(np.float64)
+    hb = h.reshape(rows, nb, 128)
+    tb = tol.reshape(rows, nb, 128)
+    # scales
+    amax_lo = np.max(np.maximum(np.abs(hb) - tb, 0.0), axis=-1)
+    amax_hi = np.max(np.abs(hb) + tb, axis=-1)
+    s_lo = f32(np.maximum(amax_lo, 1e-4) / 448.0).astype(np.float64)
+    s_hi = f32(np.maximum(amax_hi, 1e-4) / 448.0).astype(np.float64)
+    ok_s = (s_k >= s_lo) & (s_k <= s_hi)
+    assert ok_s.all(), (label, np.argwhere(~ok_s)[:5], s_k[~ok_s][:5], s_lo[~ok_s][:5], s_hi[~ok_s][:5])
+    # codes, with the kernel's scale
+    s_el = np.repeat(s_k, 128, axis=1)
+    lo = encode(f32((h - tol) / s_el))
+    hi = encode(f32((h + tol) / s_el))
+    vk, vlo, vhi = T[hq].astype(np.float64), T[lo].astype(np.float64), T[hi].astype(np.float64)
+    fixed = vlo == vhi
+    bad_fixed = fixed & (vk != vlo)
+    assert not bad_fixed.any(), (label, np.argwhere(bad_fixed)[:5], hq[bad_fixed][:5], lo[bad_fixed][:5])
+    inside = (vk >= vlo) & (vk <= vhi)
+    assert inside.all(), (label, np.argwhere(~inside)[:5])
+    return int(fixed.sum()), int(fixed.size)
+
+
+def check_call(hq, hs_bits, qa, sa, qb, sb, masked_m, tol_fn, label, min_fixed):
+    g, max_m, _ = qa.shape
+    inter = qb.shape[1] // 2
+    r, valid = oracle.grouped_masked_ref(qa, sa, qb, sb, masked_m)
+    gate, up = r[..., :inter], r[..., inter:]
+    h, _ = oracle.masked_swiglu_ref(qa, sa, qb, sb, masked_m)
+    hq_o, hs_o, _ = oracle.masked_swiglu_quant_ref(qa, sa, qb, sb, masked_m)
+    rms_g, rms_u = rms(gate[valid]), rms(up[valid])
+    fixed, total, same_code, same_scale = 0, 0, [], []
+    for e in range(g):
+        cnt = int(valid[e].sum())
+        # rows without a result and the scale padding keep their sentinels
+        assert np.all(hq[e, cnt:] == H.SENTINEL_CODE), (label, e)
+        assert np.all(hs_bits[e, :, cnt:] == H.SENTINEL_SCALE), (label, e)
+        if cnt == 0:
+            continue
+        tol = tol_fn(gate[e, :cnt], up[e, :cnt], rms_g, rms_u)
+        s_bits = np.ascontiguousarray(hs_bits[e, :, :cnt].T)
+        f, t = check_rows(hq[e, :cnt], s_bits, h[e, :cnt], tol, f"{label} expert {e}")
+        fixed, total = fixed + f, total + t
+        same_code.append(np.sum(T[hq[e, :cnt]] == T[hq_o[e, :cnt]]))
+        same_scale.append(np.sum(s_bits.view(np.float32) == hs_o[e, :cnt]))
+    n_scales = total // 128
+    share, code_share = fixed / max(total, 1), sum(same_code) / max(total, 1)
+    scale_share = sum(same_scale) / max(n_scales, 1)
+    print(f"  fixed {share:.5f} same code as the oracle {code_share:.5f} same scale {scale_share:.5f}", flush=True)
+    assert share >= min_fixed, (label, share)
+    return code_share, scale_share
+
+
+def exact_tol(gate, up, rms_g=None, rms_u=None):
+    return 2.0 ** -17 * np.abs(oracle.silu(gate) * up) + 1e-30
+
+
+@pytest.mark.parametrize("cfg", [None] + CONFIGS)
+def test_exact_inputs(gpu, cfg, monkeypatch):
+    if cfg:
+        monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    g, max_m, inter, k = 5, 300, 384, 512
+    mm = [0, 1, 77, 300, 351]  # empty, one row, ragged, full, clamped
+    qa, sa, qb, sb, mm = exact_case(g, max_m, inter, k, mm, seed=11)
+    assert_fp32_exact(qa, sa, qb, sb)
+    print(f"[case] swiglu exact {cfg}", flush=True)
+    hq, hs, fq, fs = H.run_swiglu(qa, sa, qb, sb, mm, gpu)
+    assert H.swiglu_guards_untouched(fq, fs, hq.size, hs.size)
+    # (scales are only checked against their interval: the kernel's fp32
+    # SiLU moves amax by an ulp or two, so the scale's last bits may differ)
+    code_share, _ = check_call(hq, hs, qa, sa, qb, sb, mm, exact_tol, f"exact {cfg}", 0.999)
+    assert code_share >= 0.999
+
+
+@pytest.mark.parametrize("cfg,max_m", [(None, 96), (None, 40), ("swiglu_256x256_w8_s2_pp", 300),
+                                       ("swiglu_256x256_w8_s2", 200), ("swiglu_128x256_w8_s3", 200),
+                                       ("swiglu_64x256_w4_s3", 130)])
+def test_workload_like_inputs(gpu, cfg, max_m, monkeypatch):
+    if cfg:
+        monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    g, inter, k = 6, 256, 640
+    mm = [0, 1, 17, max_m, max_m + 50, max_m // 2 + 3]
+    qa, sa, qb, sb, mm = workload_case(g, max_m, inter, k, mm, seed=5)
+    print(f"[case] swiglu workload-like {cfg} max_m={max_m}", flush=True)
+    hq, hs, fq, fs = H.run_swiglu(qa, sa, qb, sb, mm, gpu)
+    assert H.swiglu_guards_untouched(fq, fs, hq.size, hs.size)
+    code_share, _ = check_call(hq, hs, qa, sa, qb, sb, mm, rule_tol, f"workload-like {cfg}", 0.15)
+    assert code_share >= 0.98, code_share
+
+
+def test_deterministic_and_expected_m_hint(gpu):
+    g, max_m, inter, k = 3, 200, 256, 384
+    qa, sa, qb, sb, mm = workload_case(g, max_m, inter, k, [200, 5, 120], seed=8)
+    print("[case] swiglu determinism", flush=True)
+    a = H.run_swiglu(qa, sa, qb, sb, mm, gpu)
+    b = H.run_swiglu(qa, sa, qb, sb, mm, gpu, expected_m=8)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_feeds_the_second_gemm(gpu):
+    """hq/hs are the masked GEMM's A operand as they stand: FC2 over the
+    kernel's h matches FC2 over the oracle's h within the GEMM rule plus what
+    the codes the oracle leaves open can change (one e4m3 step each, and the
+    scale interval), bounded from the oracle side alone."""
+    g, max_m, inter, k, n2 = 4, 130, 384, 512, 272
+    qa, sa, qb, sb, mm = workload_case(g, max_m, inter, k, [130, 0, 64, 99], seed=21)
+    rng = np.random.default_rng(22)
+    w2 = [oracle.quantize_b_128x128((rng.standard_normal((n2, inter)) * 0.02).astype(np.float32)) for _ in range(g)]
+    q2 = np.stack([q for q, _ in w2])
+    s2 = np.stack([s for _, s in w2])
+    print("[case] swiglu -> masked GEMM chain", flush=True)
+    hq, hs, _, _ = H.run_swiglu(qa, sa, qb, sb, mm, gpu)
+    hq_o, hs_o, valid = oracle.masked_swiglu_quant_ref(qa, sa, qb, sb, mm)
+    # second GEMM on the device, straight from the fused kernel's buffers
+    import torch
+    a2 = torch.from_numpy(hq).to(gpu).view(torch.float8_e4m3fn)
+    sfa2 = torch.from_numpy(hs.view(np.float32)).to(gpu)
+    d2, _ = H.sentinel_bf16((g, max_m, n2), gpu)
+    import fp8_block_scaled_nt_amd as dg
+    dg.m_grouped_fp8_gemm_nt_masked((a2, sfa2), (H.codes_to_device(q2, gpu), H.f32_to_device(s2, gpu)), d2,
+                                    torch.from_numpy(mm).to(gpu))
+    torch.cuda.synchronize()
+    d2 = H.d_float(d2)
+    # oracle chain
+    r2, _ = oracle.grouped_masked_ref(hq_o, np.nan_to_num(hs_o), q2, s2, np.asarray(mm))
+    r, _ = oracle.grouped_masked_ref(qa, sa, qb, sb, mm)
+    h, _ = oracle.masked_swiglu_ref(qa, sa, qb, sb, mm)
+    rms_g, rms_u = rms(r[..., :inter][valid]), rms(r[..., inter:][valid])
+    rms2 = rms(r2[valid])
+    for e in range(g):
+        cnt = int(valid[e].sum())
+        if cnt == 0:
+            continue
+        tol = rule_tol(r[e, :cnt, :inter], r[e, :cnt, inter:], rms_g, rms_u)
+        hv = h[e, :cnt]
+        s_o = np.repeat(hs_o[e, :cnt].astype(np.float64), 128, axis=1)
+        # per element, how far the kernel's dequantised h can be from the
+        # oracle's: both lie within half a step of their own value of h, the
+        # kernel's h within tol of the exact one, and its scale moves with amax
+        step = np.maximum(np.abs(hv) * 2.0 ** -3, s_o * 2.0 ** -9)
+        hb = tol.reshape(cnt, -1, 128).max(axis=-1)
+        s_rel = np.repeat(hb / (448.0 * hs_o[e, :cnt]), 128, axis=1) + 2.0 ** -23
+        dh = step + 2 * tol + np.abs(hv) * 2 * s_rel
+        w = T[q2[e]].astype(np.float64) * np.repeat(s2[e], 128, axis=1)[np.arange(n2) // 128]
+        bound = dh @ np.abs(w).T
+        res = oracle.tolerance_check(d2[e, :cnt], r2[e, :cnt], rms=rms2)
+        err = np.abs(d2[e, :cnt] - r2[e, :cnt])
+        rule = oracle.check.REL_TOL * np.abs(r2[e, :cnt]) + oracle.check.ABS_TOL_RMS * rms2
+        assert np.all(err <= rule + bound), (e, float(np.max(err - rule - bound)))
+        print(f"  expert {e}: {res['n_bad']} of {res['n']} outside the plain GEMM rule", flush=True)
+
+
+def test_full_size_sampled(gpu):
+    """The SwiGLU workload (16 experts, max_m 256, 2I = 4096, I = 2048,
+    K = 7168), run as the benchmark runs it: quantised on the GPU by
+    the library, the fused kernel at its default configuration.  For four
+    experts the oracle re-quantises the expert's A rows and B on the CPU
+    (the codes and scales must be bit-identical) and computes h for the
+    first, last and a middle valid row."""
+    import torch
+
+    import fp8_block_scaled_nt_amd as dg
+    name = "moe_swiglu_16x256_i2048_k7168"
+    x = W.draw(name)
+    s = W.WORKLOADS[name].shape
+    g, max_m, inter, k = s["g"], s["max_m"], s["inter"], s["k"]
+    mm = x["masked_m"]
+    print(f"[case] swiglu full size {name}", flush=True)
+    qa, sfa = dg.quantize_a_1x128(H.f32_to_device(x["a"], gpu))
+    qb, sfb = dg.quantize_b_128x128(H.f32_to_device(x["b"], gpu))
+    ld = H.sfa_ld(max_m)
+    nq, ns, guard = g * max_m * inter, g * (inter // 128) * ld, 4096
+    fq = torch.full((nq + guard,), H.SENTINEL_CODE, dtype=torch.uint8, device=gpu)
+    fs = torch.full((ns + guard,), H.SENTINEL_SCALE, dtype=torch.int32, device=gpu)
+    hq_t = fq[:nq].view(g, max_m, inter)
+    hs_t = fs[:ns].view(torch.float32).view(g, inter // 128, ld)
+    expected = int(np.clip(mm, 0, max_m).mean())
+    dg.m_grouped_fp8_gemm_nt_masked_swiglu((qa, sfa), (qb, sfb), (hq_t.view(torch.float8_e4m3fn), hs_t),
+                                           torch.from_numpy(mm).to(gpu), expected)
+    torch.cuda.synchronize()
+    assert H.swiglu_guards_untouched(fq, fs, nq, ns)
+    hq = hq_t.cpu().numpy()
+    hs = fs[:ns].view(g, inter // 128, ld).cpu().numpy().view(np.uint32)
+    fixed, total, same = 0, 0, 0
+    for e in range(g):
+        cnt = int(min(max(mm[e], 0), max_m))
+        assert np.all(hq[e, cnt:] == H.SENTINEL_CODE)
+        assert np.all(hs[e, :, cnt:] == H.SENTINEL_SCALE)
+    for e in [int(np.argmax(mm)), int(np.argmin(np.where(mm > 0, mm, max_m + 1))), 5, 9]:
+        cnt = int(mm[e])
+        if cnt == 0:
+            continue
+        rows = np.array(sorted({0, cnt // 2, cnt - 1}))
+        qa_r, sa_r = oracle.quantize_a_1x128(x["a"][e][rows])
+        assert np.array_equal(qa[e].view(torch.uint8)[torch.from_numpy(rows).to(gpu)].cpu().numpy(), qa_r)
+        qb_e, sb_e = oracle.quantize_b_128x128(x["b"][e])
+        assert np.array_equal(qb[e].view(torch.uint8).cpu().numpy(), qb_e)
+        assert np.array_equal(sfb[e].cpu().numpy(), sb_e)
+        sub = oracle.gemm_nt_ref(qa_r, sa_r, qb_e, sb_e)
+        gate, up = sub[:, :inter], sub[:, inter:]
+        h = oracle.silu(gate) * up
+        f, t = check_rows(hq[e, rows], np.ascontiguousarray(hs[e][:, rows].T), h,
+                          rule_tol(gate, up, rms(gate), rms(up)), f"{name} expert {e}")
+        fixed, total = fixed + f, total + t
+        hq_o, _ = oracle.quantize_a_1x128(h.astype(np.float32))
+        same += int(np.sum(T[hq[e, rows]] == T[hq_o]))
+    print(f"  fixed {fixed / max(total, 1):.5f} same code as the oracle {same / max(total, 1):.5f} of {total}",
+          flush=True)
+    assert fixed >= 0.1 * total and same >= 0.98 * total

@@ -23,7 +23,7 @@ class Workload:
 
     def __init__(self, name, kind, desc, **shape):
         self.name = name
-        self.kind = kind  # "dense" | "contiguous" | "masked" | "kgrouped" | "bf16"
+        self.kind = kind  # "dense" | "contiguous" | "masked" | "kgrouped" | "bf16" | "swiglu"
         self.desc = desc
         self.shape = shape
 
@@ -49,6 +49,13 @@ WORKLOADS = {
         "moe_masked_16x256_n4096_k7168", "masked",
         "MoE grouped masked decode, 16 experts, max_m=256, N=4096 K=7168",
         g=16, max_m=256, n=4096, k=7168, b_std=0.02),
+    # MoE FC1 + SwiGLU + FP8 requantisation on the masked decode layout: the
+    # masked shape read as [gate; up] (2I = 4096 rows, I = 2048), drawn with
+    # the same seed, so its inputs equal the masked workload's
+    "moe_swiglu_16x256_i2048_k7168": Workload(
+        "moe_swiglu_16x256_i2048_k7168", "swiglu",
+        "MoE FC1 + SwiGLU + requantise, masked layout, 16 experts, max_m=256, I=2048 K=7168",
+        g=16, max_m=256, inter=2048, k=7168, b_std=0.02),
     # BF16 dense GEMM on the large dense shape (operands rounded to bf16 by
     # the caller from these fp32 draws)
     "bf16_dense_4096x7168x16384": Workload(
@@ -137,6 +144,8 @@ def draw(name, seed=0):
         return draw_contiguous(s["group_rows"], s["n"], s["k"], seed, s["b_std"])
     if w.kind == "kgrouped":
         return draw_kgrouped(s["k_sizes"], s["m"], s["n"], seed, s["b_std"])
+    if w.kind == "swiglu":
+        return draw_masked(s["g"], s["max_m"], 2 * s["inter"], s["k"], seed, s["b_std"])
     return draw_masked(s["g"], s["max_m"], s["n"], s["k"], seed, s["b_std"])
 
 
@@ -168,6 +177,16 @@ def algorithmic_work(kind, **p):
         rows = int(cnt.sum())
         experts = int((cnt > 0).sum())
         index_bytes = 4 * cnt.size
+    elif kind == "swiglu":
+        # the masked FC1 GEMM with n = 2I, writing h as e4m3 codes (1 byte)
+        # with one fp32 scale per 128 columns instead of D
+        cnt = np.clip(np.asarray(p["masked_m"], np.int64), 0, p["max_m"])
+        rows, experts = int(cnt.sum()), int((cnt > 0).sum())
+        i = n // 2
+        flops = 2.0 * rows * n * k
+        nbytes = (rows * k + 4 * rows * kb + experts * (n * k + 4 * nb * kb) + 4 * cnt.size
+                  + rows * i + 4 * rows * (i // SLAB))
+        return flops, nbytes
     elif kind == "bf16":
         # two bytes per element of A, B and D; no scales
         m = p["m"]
@@ -203,5 +222,8 @@ def workload_work(name, inputs=None):
         return algorithmic_work("bf16", m=s["m"], n=s["n"], k=s["k"])
     if w.kind == "kgrouped":
         return algorithmic_work("kgrouped", k_sizes=s["k_sizes"], m=s["m"], n=s["n"], k=int(sum(s["k_sizes"])))
+    if w.kind == "swiglu":
+        mm = inputs["masked_m"] if inputs is not None else np.random.default_rng(0).integers(0, s["max_m"] + 1, s["g"])
+        return algorithmic_work("swiglu", masked_m=mm, max_m=s["max_m"], n=2 * s["inter"], k=s["k"])
     mm = inputs["masked_m"] if inputs is not None else np.random.default_rng(0).integers(0, s["max_m"] + 1, s["g"])
     return algorithmic_work("masked", masked_m=mm, max_m=s["max_m"], n=s["n"], k=s["k"])
