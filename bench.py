@@ -54,8 +54,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--mode", choices=["bench", "counters"], default="bench",
                     help="counters: run plain kernels of known traffic (1 GiB fill, 1 GiB read; "
-                         "calibration for rocprofv3 FETCH_SIZE/WRITE_SIZE) and eager GEMM launches "
-                         "of the headline workload, print nothing")
+                         "calibration for rocprofv3 FETCH_SIZE/WRITE_SIZE), then eager GEMM launches "
+                         "of the headline workload and of the --workloads list ('main' = none), "
+                         "print nothing")
     return ap.parse_args()
 
 
@@ -302,6 +303,19 @@ def main():
         for i in range(args.kernel_launches):
             launch(rot[i])
         torch.cuda.synchronize()
+        del rot
+        torch.cuda.empty_cache()
+        names = [] if args.workloads == "main" else (
+            [x for x in W.WORKLOADS if x != MAIN_WORKLOAD] if args.workloads == "all"
+            else args.workloads.split(","))
+        for name in names:
+            _, _, rot_x, launch_x, _, inp_x = setup_workload(torch, np, dg, W, name, dev)
+            for i in range(args.kernel_launches):
+                launch_x(rot_x[i])
+            torch.cuda.synchronize()
+            print(f"[counters] {name}: {args.kernel_launches} launches", file=sys.stderr, flush=True)
+            del rot_x, inp_x
+            torch.cuda.empty_cache()
         return 0
     m, n, k = params["m"], params["n"], params["k"]
     flops, gemm_bytes = W.algorithmic_work("dense", m=m, n=n, k=k)
@@ -363,7 +377,7 @@ def main():
                        "tflops": round(tf, 1), "gbs": round(gbs, 1), "bound": bound,
                        "peak": peak_tf if bound == "mfma" else HBM_PEAK_GBS,
                        "frac": round(tf / peak_tf if bound == "mfma" else gbs / HBM_PEAK_GBS, 4),
-                       "algorithmic_flops": fl, "algorithmic_bytes": by}
+                       "algorithmic_flops": fl, "algorithmic_bytes": by, "traffic": measured_traffic(name)}
         print(f"[bench] {name}: {a_us:.1f} us, {tf:.1f} TFLOP/s, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
         del rot_x, inp_x
         torch.cuda.empty_cache()
