@@ -24,14 +24,16 @@ bf16.  Every reading is listed with its reason in the design notes.
 Modules
 -------
 e4m3   exact 256-entry decode table, round-to-nearest-even saturating encoder
-quant  1x128 (activation) and 128x128 (weight) quantisers
+e2m1   the FP4 codec (16 codes) and its two-per-byte packing
+quant  1x128 (activation) and 128x128 (weight) quantisers, FP8 and FP4
 gemm   dense, contiguous-grouped, masked-grouped and K-grouped reference GEMMs in fp64,
-       and the BF16 NT GEMM; FC1 + SwiGLU on the masked layout
+       the BF16 and FP4 NT GEMMs; FC1 + SwiGLU on the masked layout
 check  the element-wise acceptance rule
 """
 
 from .e4m3 import E4M3_MAX, decode_table, decode, encode  # noqa: F401
 from .quant import quantize_a_1x128, quantize_b_128x128  # noqa: F401
+from .quant import quantize_a_1x128_fp4, quantize_b_128x128_fp4  # noqa: F401
 from .gemm import (  # noqa: F401
     gemm_nt_ref,
     gemm_nt_ref_at,
@@ -41,6 +43,7 @@ from .gemm import (  # noqa: F401
     k_grouped_ref_at,
     bf16_gemm_nt_ref,
     bf16_to_f64,
+    fp4_gemm_nt_ref,
     masked_swiglu_quant_ref,
     masked_swiglu_ref,
     silu,

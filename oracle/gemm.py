@@ -305,3 +305,32 @@ def masked_swiglu_quant_ref(qa, sfa, qb, sfb, masked_m):
         if rows:
             hq[e, :rows], hs[e, :rows] = quantize_a_1x128(h[e, :rows].astype(np.float32))
     return hq, hs, valid
+
+
+def fp4_gemm_nt_ref(pa, sfa, pb, sfb):
+    """FP4 (e2m1) block-scaled NT GEMM in fp64: the dense FP8 method with
+    e2m1 operands (the pages name FP4 as a GEMM format, pomoai.com, core
+    functions; readings: e2m1 values, packed two per byte, with the FP8
+    scale layout: sfa M x K/128, sfb ceil(N/128) x K/128).
+
+    r[m, n] = sum over slabs kb of
+              (sum_{k in kb} a[m, k] b[n, k]) * sfa[m, kb] * sfb[n / 128, kb]
+    """
+    from .e2m1 import decode_packed
+    a = decode_packed(pa)
+    b = decode_packed(pb)
+    m, k = a.shape
+    n = b.shape[0]
+    if b.shape[1] != k or k % SLAB:
+        raise ValueError("bad operand shapes")
+    kb = k // SLAB
+    sa = np.asarray(sfa, np.float64)
+    sb = np.asarray(sfb, np.float64)
+    if sa.shape != (m, kb) or sb.shape != ((n + SLAB - 1) // SLAB, kb):
+        raise ValueError("bad scale shapes")
+    block_of_col = np.arange(n) // SLAB
+    r = np.zeros((m, n))
+    for s in range(kb):
+        cols = slice(s * SLAB, (s + 1) * SLAB)
+        r += (a[:, cols] @ b[:, cols].T) * (sa[:, s][:, None] * sb[block_of_col, s][None, :])
+    return r

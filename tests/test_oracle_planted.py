@@ -49,6 +49,15 @@ MUTATIONS = [
     # BF16: wrong half of the fp32 word, transposed operand
     ("gemm.py", "b = np.asarray(bits, np.uint16).astype(np.uint32) << 16", "b = np.asarray(bits, np.uint16).astype(np.uint32) << 15"),
     ("gemm.py", "    return a @ b.T\n", "    return a @ b[::-1].T\n"),
+    # FP4: decode exponent, tie rule, nibble order, range of the scale,
+    # B scale block of a column
+    ("e2m1.py", "(2 + f) * 2.0 ** (e - 2)", "(2 + f) * 2.0 ** (e - 1)"),
+    ("e2m1.py", "q = np.rint(np.ldexp(a, -(e - 1)))", "q = np.floor(np.ldexp(a, -(e - 1)) + 0.5)"),
+    ("e2m1.py", "out[..., 0::2] = p & 0xF\n    out[..., 1::2] = p >> 4", "out[..., 1::2] = p & 0xF\n    out[..., 0::2] = p >> 4"),
+    ("quant.py", "s = (amax / np.float32(E2M1_MAX)).astype(np.float32)\n    scaled",
+     "s = (amax / np.float32(E2M1_MAX + 1)).astype(np.float32)\n    scaled"),
+    ("gemm.py", "(sa[:, s][:, None] * sb[block_of_col, s][None, :])\n    return r\n",
+     "(sa[:, s][:, None] * sb[0, s][None])\n    return r\n"),
     # e4m3: tie rule, exponent bias, saturation code, subnormal boundary
     ("e4m3.py", "q = np.rint(steps)", "q = np.floor(steps + 0.5)"),
     ("e4m3.py", "mag = (8 + f) * 2.0 ** (e - 10)", "mag = (8 + f) * 2.0 ** (e - 9)"),
@@ -66,7 +75,8 @@ MUTATIONS = [
      "amax = np.max(np.abs(blk), axis=(2,)).max(axis=0) * np.float32(0.999)"),
 ]
 
-PIN_TESTS = ["test_oracle_e4m3.py", "test_oracle_quant.py", "test_oracle_gemm.py", "test_accounting.py"]
+PIN_TESTS = ["test_oracle_e4m3.py", "test_oracle_quant.py", "test_oracle_gemm.py", "test_oracle_fp4.py",
+             "test_accounting.py"]
 
 
 def _run_one(case, base):
