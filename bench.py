@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16 MFMA
+FP4_PEAK_TFLOPS = 10100.0      # MI355X dense FP4 MFMA
 ROTATE_BYTES = 600 << 20       # > 2x the 256 MiB Infinity Cache
 MAIN_WORKLOAD = "dense_decode_64x2112x7168"
 CALIB_BYTES = 1 << 30          # plain-kernel traffic for the counter calibration
@@ -180,6 +181,23 @@ def setup_workload(torch, np, dg, W, name, dev):
 
         def launch(st):
             dg.bf16_gemm_nt(st["a"], st["b"], st["d"])
+
+        return w.kind, dict(m=m, n=n, k=k), rot, launch, None, inp
+    if w.kind == "fp4":
+        m, n, k = s["m"], s["n"], s["k"]
+        qa, sfa = dg.quantize_a_1x128_fp4(torch.from_numpy(inp["a"]).to(dev))
+        qb, sfb = dg.quantize_b_128x128_fp4(torch.from_numpy(inp["b"]).to(dev))
+
+        def make(i):
+            d = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            if i == 0:
+                return {"qa": qa, "sfa": sfa, "qb": qb, "sfb": sfb, "d": d}
+            return {"qa": qa.clone(), "sfa": sfa.clone(), "qb": qb.clone(), "sfb": sfb.clone(), "d": d}
+
+        rot = Rotation(make, qa.numel() + qb.numel() + 2 * m * n)
+
+        def launch(st):
+            dg.fp4_gemm_nt((st["qa"], st["sfa"]), (st["qb"], st["sfb"]), st["d"])
 
         return w.kind, dict(m=m, n=n, k=k), rot, launch, None, inp
     if w.kind == "kgrouped":
@@ -371,7 +389,7 @@ def main():
         a_us, md_us = kernel_time_us(torch, dg, launch_x, rot_x, max(10, args.kernel_launches // 4))
         tf = fl / (a_us * 1e-6) / 1e12
         gbs = by / (a_us * 1e-6) / 1e9
-        peak_tf = BF16_PEAK_TFLOPS if kind_x == "bf16" else FP8_PEAK_TFLOPS
+        peak_tf = {"bf16": BF16_PEAK_TFLOPS, "fp4": FP4_PEAK_TFLOPS}.get(kind_x, FP8_PEAK_TFLOPS)
         bound = "mfma" if fl / by > peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
         extra[name] = {"kernel_avg_us": round(a_us, 2), "kernel_median_us": round(md_us, 2),
                        "tflops": round(tf, 1), "gbs": round(gbs, 1), "bound": bound,

@@ -13,6 +13,8 @@ Layouts (all row-major, packed):
   sfb  fp32 [ceil(n/128), k/128]; grouped: [g, ceil(n/128), k/128]
   d    bf16 [m, n]; masked: [g, max_m, n]
   hq   (SwiGLU) e4m3 [g, max_m, inter]; hs fp32 [g, inter/128, get_sfa_ld(max_m)]
+  FP4  a [m, k/2], b [n, k/2] uint8, two e2m1 codes per byte (low nibble first),
+       with the FP8 scale layouts
 """
 
 import ctypes
@@ -26,7 +28,7 @@ LIB_PATH = os.path.join(_PKG_DIR, "libdg.so")
 __all__ = [
     "DGError", "lib", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous",
     "m_grouped_fp8_gemm_nt_masked", "m_grouped_fp8_gemm_nt_masked_swiglu", "quantize_a_1x128", "quantize_b_128x128",
-    "k_grouped_fp8_gemm_nt", "bf16_gemm_nt", "get_m_alignment_for_contiguous_layout", "get_sfa_ld", "empty_sfa",
+    "k_grouped_fp8_gemm_nt", "bf16_gemm_nt", "fp4_gemm_nt", "quantize_a_1x128_fp4", "quantize_b_128x128_fp4", "get_m_alignment_for_contiguous_layout", "get_sfa_ld", "empty_sfa",
     "profile_next_launch",
     "reserve_workspace",
 ]
@@ -49,6 +51,9 @@ _SIGNATURES = {
     "dg_m_grouped_fp8_gemm_nt_masked_swiglu": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _vp],
     "dg_k_grouped_fp8_gemm_nt": [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _vp],
     "dg_bf16_gemm_nt": [_vp, _vp, _vp, _ci, _ci, _ci, _vp],
+    "dg_fp4_gemm_nt": [_vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _vp],
+    "dg_quantize_a_1x128_fp4": [_vp, _vp, _vp, _ci, _ci, _vp],
+    "dg_quantize_b_128x128_fp4": [_vp, _vp, _vp, _ci, _ci, _vp],
     "dg_get_m_alignment_for_contiguous_layout": [],
     "dg_get_sfa_ld": [_ci],
     "dg_quantize_a_1x128": [_vp, _vp, _vp, _ci, _ci, _vp],
@@ -306,4 +311,54 @@ def quantize_b_128x128(x, q=None, sfb=None):
     if tuple(q.shape) != (n, k) or tuple(sfb.shape) != ((n + 127) // 128, k // 128):
         raise ValueError("output shape mismatch")
     _check(lib().dg_quantize_b_128x128(_ptr(x), _ptr(q), _ptr(sfb), n, k, _stream()))
+    return q, sfb
+
+
+def fp4_gemm_nt(a_pair, b_pair, d):
+    """FP4 NT GEMM: a (uint8 [m, k/2], two e2m1 codes per byte) with sfa
+    (slab-major [k/128, get_sfa_ld(m)]), b (uint8 [n, k/2]) with sfb
+    ([ceil(n/128), k/128]); d is bf16 [m, n], written in place."""
+    a, sfa = a_pair
+    b, sfb = b_pair
+    _need(a, "a", (torch.uint8,), 2)
+    _need(b, "b", (torch.uint8,), 2)
+    _need(d, "d", (torch.bfloat16,), 2)
+    _need(sfa, "sfa", (torch.float32,), 2)
+    _need(sfb, "sfb", (torch.float32,), 2)
+    m, kh = a.shape
+    n = b.shape[0]
+    k = 2 * kh
+    if b.shape[1] != kh or tuple(d.shape) != (m, n):
+        raise ValueError(f"shape mismatch a{tuple(a.shape)} b{tuple(b.shape)} d{tuple(d.shape)}")
+    if tuple(sfa.shape) != (k // 128, get_sfa_ld(m)) or tuple(sfb.shape) != ((n + 127) // 128, k // 128):
+        raise ValueError("scale shape mismatch")
+    _check(lib().dg_fp4_gemm_nt(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(d), m, n, k, _stream()))
+    return d
+
+
+def quantize_a_1x128_fp4(x, q=None, sfa=None):
+    """fp32 [m, k] -> (packed e2m1 codes uint8 [m, k/2], slab-major sfa)."""
+    _need(x, "x", (torch.float32,), 2)
+    m, k = x.shape
+    q = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device) if q is None else q
+    sfa = empty_sfa(m, k, None, x.device) if sfa is None else sfa
+    _need(q, "q", (torch.uint8,), 2)
+    _need(sfa, "sfa", (torch.float32,), 2)
+    if tuple(q.shape) != (m, k // 2) or tuple(sfa.shape) != (k // 128, get_sfa_ld(m)):
+        raise ValueError("output shape mismatch")
+    _check(lib().dg_quantize_a_1x128_fp4(_ptr(x), _ptr(q), _ptr(sfa), m, k, _stream()))
+    return q, sfa
+
+
+def quantize_b_128x128_fp4(x, q=None, sfb=None):
+    """fp32 [n, k] -> (packed e2m1 codes uint8 [n, k/2], sfb [ceil(n/128), k/128])."""
+    _need(x, "x", (torch.float32,), 2)
+    n, k = x.shape
+    q = torch.empty((n, k // 2), dtype=torch.uint8, device=x.device) if q is None else q
+    sfb = torch.empty(((n + 127) // 128, k // 128), dtype=torch.float32, device=x.device) if sfb is None else sfb
+    _need(q, "q", (torch.uint8,), 2)
+    _need(sfb, "sfb", (torch.float32,), 2)
+    if tuple(q.shape) != (n, k // 2) or tuple(sfb.shape) != ((n + 127) // 128, k // 128):
+        raise ValueError("output shape mismatch")
+    _check(lib().dg_quantize_b_128x128_fp4(_ptr(x), _ptr(q), _ptr(sfb), n, k, _stream()))
     return q, sfb

@@ -100,7 +100,7 @@ template <int BM, int BN, int WM, int WN, int NST, int VAR, int SCHED = dg::kInt
 Config make_config(const char* name) {
   return Config{name, VAR, BM, BN, WM, WN, NST, SCHED, DT, EPI,
                 reinterpret_cast<const void*>(&dg::gemm_fp8_nt_kernel<BM, BN, WM, WN, NST, VAR, SCHED, DT, EPI>),
-                dg::Smem<BM, BN, NST>::kBytes};
+                dg::Smem<BM, BN, NST, DT == dg::kFp4 ? 2 : 1>::kBytes};
 }
 
 const Config* configs(int* count) {
@@ -143,6 +143,10 @@ const Config* configs(int* count) {
       make_config<256, 256, 2, 4, 2, dg::kDense, dg::kInterleaved, dg::kBf16>("bf16_256x256_w8_s2"),
       make_config<128, 128, 2, 2, 2, dg::kDense, dg::kInterleaved, dg::kBf16>("bf16_128x128_w4_s2"),
       make_config<64, 32, 2, 2, 4, dg::kDense, dg::kInterleaved, dg::kBf16>("bf16_64x32_w4_s4"),
+      // FP4 (e2m1) dense
+      make_config<256, 256, 2, 4, 2, dg::kDense, dg::kInterleaved, dg::kFp4>("fp4_256x256_w8_s2"),
+      make_config<128, 128, 2, 2, 2, dg::kDense, dg::kInterleaved, dg::kFp4>("fp4_128x128_w4_s2"),
+      make_config<64, 32, 2, 2, 4, dg::kDense, dg::kInterleaved, dg::kFp4>("fp4_64x32_w4_s4"),
       // MoE FC1 + SwiGLU + FP8 requantisation, masked layout (a 256-column
       // tile = 128 gate + 128 up columns = one 128-wide block of h)
       make_config<256, 256, 2, 4, 2, dg::kMasked, dg::kPingPong, dg::kFp8, dg::kEpiSwigluFp8>("swiglu_256x256_w8_s2_pp"),
@@ -252,6 +256,7 @@ void fill_common(dg::GemmParams& p, const Config& c, int m, int n, int k) {
   p.n = n;
   p.k = k;
   p.kb_count = k / 128;
+  p.sk_count = p.kb_count;
   p.nb_count = (n + 127) / 128;
   p.sfa_ld = sfa_ld(m);
   p.tiles_m = (m + c.bm - 1) / c.bm;
@@ -276,12 +281,14 @@ int check_rows(long long rows, int k) {
   return DG_OK;
 }
 
-// Dense launch with the split-K choice, shared by the fp8 and bf16 entry
-// points; k_bytes is K in bytes (one per fp8 value, two per bf16 value).
+// Dense launch with the split-K choice, shared by the fp8, bf16 and fp4 entry
+// points; k_bytes is K in bytes (one per fp8 value, two per bf16 value, half
+// per fp4 value) and scale_slabs the number of 128-wide scale slabs of K.
 int launch_dense(const Config* c, dg::GemmParams& p, int dev, const DeviceInfo* info, int m, int n, int k_bytes,
-                 dg_stream_t stream) {
+                 int scale_slabs, dg_stream_t stream) {
   p.num_groups = 1;
   fill_common(p, *c, m, n, k_bytes);
+  p.sk_count = scale_slabs;
   p.num_tiles = p.tiles_m * p.tiles_n;
   p.splits = 1;
   p.split_slabs = p.kb_count;
@@ -314,6 +321,47 @@ int launch_dense(const Config* c, dg::GemmParams& p, int dev, const DeviceInfo* 
   }
   return launch(*c, p, p.num_tiles * p.splits, (hipStream_t)stream);
 }
+
+int quantize_a(const void* kernel, const float* x, uint8_t* q, float* sfa, int m, int k, dg_stream_t stream) {
+  if (!x || !q || !sfa) return fail(DG_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (m < 0) return fail(DG_ERR_INVALID_ARGUMENT, "m must be >= 0 (got %d)", m);
+  if (k < 128 || k % 128 != 0)
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "k must be a positive multiple of 128 (got %d)", k);
+  if (!aligned16(x) || !aligned16(q) || !aligned16(sfa))
+    return fail(DG_ERR_MISALIGNED, "pointers must be 16-byte aligned");
+  if (m == 0) return ok();
+  int dev;
+  DeviceInfo* info;
+  if (int s = current_device(&dev, &info)) return s;
+  const int ld = sfa_ld(m);
+  const long long units = (long long)ld * ((k / 128 + 1) / 2);
+  const long long grid = (units + 3) / 4;
+  if (grid > 0x7fffffffLL) return fail(DG_ERR_UNSUPPORTED_SHAPE, "matrix too large");
+  void* args[] = {&x, &q, &sfa, &m, &k, (void*)&ld};
+  hipError_t e = hipLaunchKernel(kernel, dim3((unsigned)grid), dim3(256), args, 0, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(DG_ERR_HIP, "quant_a launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int quantize_b(const void* kernel, const float* x, uint8_t* q, float* sfb, int n, int k, dg_stream_t stream) {
+  if (!x || !q || !sfb) return fail(DG_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (n < 0) return fail(DG_ERR_INVALID_ARGUMENT, "n must be >= 0 (got %d)", n);
+  if (k < 128 || k % 128 != 0)
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "k must be a positive multiple of 128 (got %d)", k);
+  if (!aligned16(x) || !aligned16(q) || !aligned16(sfb))
+    return fail(DG_ERR_MISALIGNED, "pointers must be 16-byte aligned");
+  if (n == 0) return ok();
+  int dev;
+  DeviceInfo* info;
+  if (int s = current_device(&dev, &info)) return s;
+  const long long grid = (long long)((n + 127) / 128) * (k / 128);
+  if (grid > 0x7fffffffLL) return fail(DG_ERR_UNSUPPORTED_SHAPE, "matrix too large");
+  void* args[] = {&x, &q, &sfb, &n, &k};
+  hipError_t e = hipLaunchKernel(kernel, dim3((unsigned)grid), dim3(256), args, 0, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(DG_ERR_HIP, "quant_b launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 
 }  // namespace
 
@@ -377,7 +425,7 @@ int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const f
   }
   dg::GemmParams p{};
   p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d;
-  return launch_dense(c, p, dev, info, m, n, k, stream);
+  return launch_dense(c, p, dev, info, m, n, k, k / 128, stream);
 }
 
 int dg_bf16_gemm_nt(const uint16_t* a, const uint16_t* b, uint16_t* d, int m, int n, int k, dg_stream_t stream) {
@@ -404,7 +452,34 @@ int dg_bf16_gemm_nt(const uint16_t* a, const uint16_t* b, uint16_t* d, int m, in
   p.a = reinterpret_cast<const uint8_t*>(a);
   p.b = reinterpret_cast<const uint8_t*>(b);
   p.d = d;
-  return launch_dense(c, p, dev, info, m, n, 2 * k, stream);
+  return launch_dense(c, p, dev, info, m, n, 2 * k, 0, stream);
+}
+
+int dg_fp4_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb, uint16_t* d, int m,
+                   int n, int k, dg_stream_t stream) {
+  if (!a || !sfa || !b || !sfb || !d) return fail(DG_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (m < 0) return fail(DG_ERR_INVALID_ARGUMENT, "m must be >= 0 (got %d)", m);
+  if (n < 1) return fail(DG_ERR_INVALID_ARGUMENT, "n must be >= 1 (got %d)", n);
+  if (k < 256 || k % 256 != 0)
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "k must be a positive multiple of 256 (got %d)", k);
+  if (int s = check_k_n(n, k / 2)) return s;
+  if (int s = check_rows(m, k / 2)) return s;
+  if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d))
+    return fail(DG_ERR_MISALIGNED, "pointers must be 16-byte aligned");
+  if (m == 0) return ok();
+  int dev;
+  DeviceInfo* info;
+  if (int s = current_device(&dev, &info)) return s;
+  const Config* c;
+  if (int s = forced_config(dg::kDense, &c, dg::kFp4)) return s;
+  if (!c) {
+    if (m <= 64) c = find_config("fp4_64x32_w4_s4", dg::kDense, dg::kFp4);
+    else if (m <= 256 || n <= 256) c = find_config("fp4_128x128_w4_s2", dg::kDense, dg::kFp4);
+    else c = find_config("fp4_256x256_w8_s2", dg::kDense, dg::kFp4);
+  }
+  dg::GemmParams p{};
+  p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d;
+  return launch_dense(c, p, dev, info, m, n, k / 2, k / 128, stream);
 }
 
 int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b,
@@ -529,45 +604,19 @@ int dg_m_grouped_fp8_gemm_nt_masked_swiglu(const uint8_t* a, const float* sfa, c
 }
 
 int dg_quantize_a_1x128(const float* x, uint8_t* q, float* sfa, int m, int k, dg_stream_t stream) {
-  if (!x || !q || !sfa) return fail(DG_ERR_INVALID_ARGUMENT, "null pointer argument");
-  if (m < 0) return fail(DG_ERR_INVALID_ARGUMENT, "m must be >= 0 (got %d)", m);
-  if (k < 128 || k % 128 != 0)
-    return fail(DG_ERR_UNSUPPORTED_SHAPE, "k must be a positive multiple of 128 (got %d)", k);
-  if (!aligned16(x) || !aligned16(q) || !aligned16(sfa))
-    return fail(DG_ERR_MISALIGNED, "pointers must be 16-byte aligned");
-  if (m == 0) return ok();
-  int dev;
-  DeviceInfo* info;
-  if (int s = current_device(&dev, &info)) return s;
-  const int ld = sfa_ld(m);
-  const long long units = (long long)ld * ((k / 128 + 1) / 2);
-  const long long grid = (units + 3) / 4;
-  if (grid > 0x7fffffffLL) return fail(DG_ERR_UNSUPPORTED_SHAPE, "matrix too large");
-  hipLaunchKernelGGL(dg::quant_a_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, x, q, sfa,
-                     m, k, ld);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(DG_ERR_HIP, "quant_a launch failed: %s", hipGetErrorString(e));
-  return ok();
+  return quantize_a(reinterpret_cast<const void*>(&dg::quant_a_kernel), x, q, sfa, m, k, stream);
 }
 
 int dg_quantize_b_128x128(const float* x, uint8_t* q, float* sfb, int n, int k, dg_stream_t stream) {
-  if (!x || !q || !sfb) return fail(DG_ERR_INVALID_ARGUMENT, "null pointer argument");
-  if (n < 0) return fail(DG_ERR_INVALID_ARGUMENT, "n must be >= 0 (got %d)", n);
-  if (k < 128 || k % 128 != 0)
-    return fail(DG_ERR_UNSUPPORTED_SHAPE, "k must be a positive multiple of 128 (got %d)", k);
-  if (!aligned16(x) || !aligned16(q) || !aligned16(sfb))
-    return fail(DG_ERR_MISALIGNED, "pointers must be 16-byte aligned");
-  if (n == 0) return ok();
-  int dev;
-  DeviceInfo* info;
-  if (int s = current_device(&dev, &info)) return s;
-  const long long grid = (long long)((n + 127) / 128) * (k / 128);
-  if (grid > 0x7fffffffLL) return fail(DG_ERR_UNSUPPORTED_SHAPE, "matrix too large");
-  hipLaunchKernelGGL(dg::quant_b_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, x, q, sfb,
-                     n, k);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(DG_ERR_HIP, "quant_b launch failed: %s", hipGetErrorString(e));
-  return ok();
+  return quantize_b(reinterpret_cast<const void*>(&dg::quant_b_kernel), x, q, sfb, n, k, stream);
+}
+
+int dg_quantize_a_1x128_fp4(const float* x, uint8_t* q, float* sfa, int m, int k, dg_stream_t stream) {
+  return quantize_a(reinterpret_cast<const void*>(&dg::quant_a_fp4_kernel), x, q, sfa, m, k, stream);
+}
+
+int dg_quantize_b_128x128_fp4(const float* x, uint8_t* q, float* sfb, int n, int k, dg_stream_t stream) {
+  return quantize_b(reinterpret_cast<const void*>(&dg::quant_b_fp4_kernel), x, q, sfb, n, k, stream);
 }
 
 }  // extern "C"

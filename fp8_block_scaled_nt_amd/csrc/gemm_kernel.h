@@ -50,9 +50,10 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) const void* glb_ptr_t;
 
 enum Variant { kDense = 0, kContiguous = 1, kMasked = 2, kKGrouped = 3 };
-// Operand type: e4m3 with block scales, or bf16 without scales (a 128-byte
-// slab row then holds 64 K values).
-enum DType { kFp8 = 0, kBf16 = 1 };
+// Operand type: e4m3 with block scales, bf16 without scales (a 128-byte slab
+// row then holds 64 K values), or e2m1 (FP4, two per byte) with block scales
+// (a 128-byte slab row then holds 256 K values: two scale slabs).
+enum DType { kFp8 = 0, kBf16 = 1, kFp4 = 2 };
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 // Epilogue: store D as bf16, or (MoE FC1 on the masked layout) pair each
 // gate column with its up column, apply SwiGLU and quantise h with the 1 x 128
@@ -82,7 +83,8 @@ struct GemmParams {
   int m;                     // rows of A (dense, contiguous) or max_m (masked)
   int n;
   int k;
-  int kb_count;              // k / 128
+  int kb_count;              // 128-byte K slabs per row (fp8: k / 128)
+  int sk_count;              // 128-wide scale slabs per row (fp8: kb_count, fp4: 2 kb_count)
   int nb_count;              // ceil(n / 128)
   int sfa_ld;                // leading dimension of slab-major sfa
   int num_groups;
@@ -186,6 +188,15 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// FP4: format 4 (e2m1) for both operands; a lane's 32 K values are 16 bytes,
+// the low four dwords of the operand (the instruction reads only those).
+__device__ __forceinline__ v4f mfma_fp4_16x16x128(const v4i& a, const v4i& b) {
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  const v8i a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+  const v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, zero, 4, 4, 0, 127, 0, 127);
+}
+
 __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b) {
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
   // fmt 0 = e4m3 for both operands; E8M0 scale 127 = 2^0 (neutral).
@@ -193,15 +204,16 @@ __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b) {
 }
 
 // LDS layout: NST stages, each holding one slab of the A tile, of the B
-// tile, the A row scales and the B block scales of that slab; the epilogue
-// reuses the space for the bf16 output tile.
-template <int BM, int BN, int NST>
+// tile, the A row scales and the B block scales of that slab (SPS scale
+// slabs per stage: 2 for FP4); the epilogue reuses the space for the bf16
+// output tile.
+template <int BM, int BN, int NST, int SPS = 1>
 struct Smem {
   static constexpr int kA = BM * kSlab;
   static constexpr int kB = BN * kSlab;
-  static constexpr int kSa = BM * 4;
+  static constexpr int kSa = BM * 4 * SPS;
   static constexpr int kSbCount = BN / 128 + 2;  // 128-row blocks a BN-wide tile can touch
-  static constexpr int kSb = 256;                // one dword DMA instruction's footprint
+  static constexpr int kSb = 256 * SPS;          // one dword DMA instruction's footprint per scale slab
   static constexpr int kStage = kA + kB + kSa + kSb;
   static constexpr int kOutPitch = BN * 2 + 16;  // bf16 output row pitch (bytes)
   static constexpr int kOut = BM * kOutPitch;
@@ -253,7 +265,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   constexpr int FM = TM / 16, FN = TN / 16;
   constexpr int kJa = BM / 8;  // DMA instructions per slab for A (1 KiB each)
   constexpr int kJb = BN / 8;
-  using S = Smem<BM, BN, NST>;
+  constexpr int kSps = DT == kFp4 ? 2 : 1;  // scale slabs per 128-byte slab
+  using S = Smem<BM, BN, NST, kSps>;
   static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be whole fragments");
   static_assert(BM <= kThreads, "row-tag pass needs one thread per tile row");
   static_assert(NST >= 2, "pipeline shape");
@@ -262,6 +275,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   // its last TN / 2 the matching up rows, so gate and up meet in one lane.
   static_assert(EPI == kEpiBf16 || (VAR == kMasked && DT == kFp8 && BN == 256 && TN % 32 == 0),
                 "SwiGLU epilogue shape");
+  static_assert(DT != kFp4 || (VAR == kDense && SCHED == kInterleaved && EPI == kEpiBf16),
+                "the FP4 path is the dense interleaved GEMM");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_flag;  // contiguous: block expert; split-K: last-arriver flag
@@ -322,19 +337,19 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
     if (expert < 0) return;  // a block of padding rows only
     if (threadIdx.x < BM) s_row_ok[threadIdx.x] = (tag == expert);
     B += (size_t)expert * p.n * p.k;
-    SFB += (size_t)expert * p.nb_count * p.kb_count;
+    SFB += (size_t)expert * p.nb_count * p.sk_count;
   } else if (VAR == kMasked) {
     int cnt = p.masked_m[g];
     cnt = cnt < 0 ? 0 : (cnt > p.m ? p.m : cnt);
     if (m0 >= cnt) return;  // masked early exit: nothing valid in this tile
     valid_rows = cnt;
     A += (size_t)g * p.m * p.k;
-    SFA += (size_t)g * p.kb_count * p.sfa_ld;
+    SFA += (size_t)g * p.sk_count * p.sfa_ld;
     B += (size_t)g * p.n * p.k;
-    SFB += (size_t)g * p.nb_count * p.kb_count;
+    SFB += (size_t)g * p.nb_count * p.sk_count;
     D += (size_t)g * p.m * p.n;
   }
-  // K slabs of this workgroup: [kb0, kb0 + KB) (KB is local; p.kb_count is K/128)
+  // K slabs of this workgroup: [kb0, kb0 + KB) (KB is local; p.kb_count counts the row's 128-byte slabs)
   int kb0 = split * p.split_slabs;
   int KB = p.splits > 1 ? min(p.split_slabs, p.kb_count - kb0) : p.kb_count;
   if (VAR == kKGrouped) {
@@ -410,19 +425,21 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   {
     int blk = EPI == kEpiSwigluFp8 ? (lane == 0 ? tn : (p.inter >> 7) + tn) : nb0 + lane;
     blk = blk < p.nb_count ? blk : p.nb_count - 1;
-    sb_off = (uint32_t)blk * (uint32_t)p.kb_count;  // sfb row stride: all K slabs
+    sb_off = (uint32_t)blk * (uint32_t)p.sk_count;  // sfb row stride: all K scale slabs
   }
-  const int c_loads = a_live + b_live + (DT == kFp8 ? 2 : 0);
+  // scale loads per slab: row and block scales of each of its scale slabs
+  constexpr int kScaleDma = DT == kBf16 ? 0 : 2 * kSps;  // bf16 operands carry no scales
+  const int c_loads = a_live + b_live + kScaleDma;
 
   // Buffer descriptors of this tile's operands (sizes in bytes; the host
   // keeps every operand below 4 GiB).
   const v4i_rsrc rs_a = make_rsrc(A, (uint32_t)row_limit * (uint32_t)K);
   const v4i_rsrc rs_b = make_rsrc(B, (uint32_t)p.n * (uint32_t)K);
-  const v4i_rsrc rs_sa = make_rsrc(SFA, (uint32_t)p.kb_count * (uint32_t)p.sfa_ld * 4u);
-  const v4i_rsrc rs_sb = make_rsrc(SFB, (uint32_t)p.nb_count * (uint32_t)p.kb_count * 4u);
+  const v4i_rsrc rs_sa = make_rsrc(SFA, (uint32_t)p.sk_count * (uint32_t)p.sfa_ld * 4u);
+  const v4i_rsrc rs_sb = make_rsrc(SFB, (uint32_t)p.nb_count * (uint32_t)p.sk_count * 4u);
   // DMA instruction d (0 .. kNumDma-1) of this wave for slab kl into stage
-  // buf: the A rows, then the B rows, then the two scale loads.
-  constexpr int kScaleDma = DT == kFp8 ? 2 : 0;  // bf16 operands carry no scales
+  // buf: the A rows, then the B rows, then the scale loads (row scales and
+  // block scales of each scale slab of the slab).
   constexpr int kNumDma = kPerWaveA + kPerWaveB + kScaleDma;
   auto issue_one = [&](int kl, int buf, int d) {
     const int kb = kb0 + kl;  // global slab index
@@ -437,10 +454,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
       const int j = jj * kWaves + wave;
       if (kJb % kWaves != 0 && j >= kJb) return;
       lds_dma16(rs_b, b_off[jj], (uint32_t)kb * kSlab, st + S::kA + j * kDmaBytes);
-    } else if (d == kPerWaveA + kPerWaveB) {
-      if (sa_lane) lds_dma4(rs_sa, sa_off * 4u, (uint32_t)kb * (uint32_t)p.sfa_ld * 4u, st + S::kA + S::kB + sa_blk * 256);
     } else {
-      if (sb_lane) lds_dma4(rs_sb, sb_off * 4u, (uint32_t)kb * 4u, st + S::kA + S::kB + S::kSa);
+      const int e = d - kPerWaveA - kPerWaveB;
+      const int h = e >> 1;                 // scale slab of this slab
+      const uint32_t ss = (uint32_t)(kb * kSps + h);
+      if ((e & 1) == 0) {
+        if (sa_lane)
+          lds_dma4(rs_sa, sa_off * 4u, ss * (uint32_t)p.sfa_ld * 4u, st + S::kA + S::kB + h * BM * 4 + sa_blk * 256);
+      } else {
+        if (sb_lane) lds_dma4(rs_sb, sb_off * 4u, ss * 4u, st + S::kA + S::kB + S::kSa + h * 256);
+      }
     }
   };
   auto issue_slab = [&](int kl, int buf) {
@@ -649,7 +672,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
 
       float sbv[FN];
       #pragma unroll
-      for (int j = 0; j < FN; ++j) sbv[j] = DT == kFp8 ? sSb[kSbUniform ? sb_idx[0] : sb_idx[j]] : 0.f;
+      for (int j = 0; j < FN; ++j) sbv[j] = DT != kBf16 ? sSb[kSbUniform ? sb_idx[0] : sb_idx[j]] : 0.f;
 
       v8i bf[FN];
       #pragma unroll
@@ -671,13 +694,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
       constexpr int F = FM * FN;
       v8i abuf[kAbuf];
       v4f sabuf[kSabuf];
+      v4f sabuf1[DT == kFp4 ? kSabuf : 1];  // FP4: row scales of the second scale slab
       v4f pr[kLag + 1];
       auto load_a = [&](int i) {
         const int f = wm * FM + i;
         const v4i lo = *(const v4i*)(sA + f * 2048 + frag_lo);
         const v4i hi = *(const v4i*)(sA + f * 2048 + frag_hi);
         abuf[i % kAbuf] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        if constexpr (DT == kFp8) sabuf[i % kSabuf] = *(const v4f*)(sSa + wm * TM + i * 16 + 4 * (lane >> 4));
+        if constexpr (DT != kBf16) sabuf[i % kSabuf] = *(const v4f*)(sSa + wm * TM + i * 16 + 4 * (lane >> 4));
+        if constexpr (DT == kFp4) sabuf1[i % kSabuf] = *(const v4f*)(sSa + BM + wm * TM + i * 16 + 4 * (lane >> 4));
       };
       #pragma unroll
       for (int i = 0; i < kPf; ++i)
@@ -700,6 +725,38 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
           #pragma unroll
           for (int j = 0; j < FN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi8(abuf[i % kAbuf]), hi8(bf[j]), acc[i][j], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        continue;
+      }
+      if constexpr (DT == kFp4) {
+        // FP4: the low 16 bytes of every fragment read lie in the slab's
+        // first 64 bytes (its first scale slab, K 0..127 of the 256), the
+        // high 16 bytes in the second; one FP4 MFMA per half, each promoted
+        // with the scales of its own scale slab.  All MFMAs of an A fragment
+        // are issued before its promotions.
+        float sbv1[FN];
+        #pragma unroll
+        for (int j = 0; j < FN; ++j) sbv1[j] = sSb[64 + (kSbUniform ? sb_idx[0] : sb_idx[j])];
+        auto lo4 = [](const v8i& x) { return v4i{x[0], x[1], x[2], x[3]}; };
+        auto hi4 = [](const v8i& x) { return v4i{x[4], x[5], x[6], x[7]}; };
+        #pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          if (i + kPf < FM) load_a(i + kPf);
+          v4f p0[FN], p1[FN];
+          #pragma unroll
+          for (int j = 0; j < FN; ++j) p0[j] = mfma_fp4_16x16x128(lo4(abuf[i % kAbuf]), lo4(bf[j]));
+          #pragma unroll
+          for (int j = 0; j < FN; ++j) p1[j] = mfma_fp4_16x16x128(hi4(abuf[i % kAbuf]), hi4(bf[j]));
+          const v4f sa0 = sabuf[i % kSabuf], sa1 = sabuf1[i % kSabuf];
+          #pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const v4f sc0 = sa0 * sbv[j];
+            const v4f sc1 = sa1 * sbv1[j];
+            #pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[i][j][e] = __builtin_fmaf(p1[j][e], sc1[e], __builtin_fmaf(p0[j][e], sc0[e], acc[i][j][e]));
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
         continue;

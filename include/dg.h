@@ -156,6 +156,24 @@ int dg_m_grouped_fp8_gemm_nt_masked_swiglu(const uint8_t* a, const float* sfa, c
 int dg_bf16_gemm_nt(const uint16_t* a, const uint16_t* b, uint16_t* d, int m, int n, int k, dg_stream_t stream);
 
 /*
+ * FP4 NT GEMM ("DeepGEMM: making LLM matrix multiplication fly", pomoai.com,
+ * core functions: FP4 named beside FP8 and BF16; its caveats warn that FP4
+ * may cost accuracy).  The pages give FP4 no scaling rule, so the FP8 method
+ * carries over with e2m1 operands:
+ *
+ *   D[m][n] = bf16( sum over slabs kb of
+ *                   (sum_{k in kb} A[m, k] * B[n, k]) * sfa[m, kb] * sfb[n / 128, kb] )
+ *
+ * A [m][k/2] and B [n][k/2] hold e2m1 codes two per byte (element 2i in the
+ * low nibble of byte i); sfa (slab-major, dg_get_sfa_ld(m)) and sfb
+ * ([ceil(n/128)][k/128]) are the FP8 scale layouts.  k must be a positive
+ * multiple of 256 (whole 128-byte rows); otherwise as dg_fp8_gemm_nt (m may
+ * be 0, n >= 1, 16-byte aligned pointers, the split-K workspace note).
+ */
+int dg_fp4_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb, uint16_t* d,
+                   int m, int n, int k, dg_stream_t stream);
+
+/*
  * K-grouped GEMM ("DeepGEMM: making LLM matrix multiplication fly",
  * pomoai.com, core functions: the K-grouped family beside the M-grouped one,
  * for the irregular shapes of MoE training such as weight gradients, where
@@ -200,6 +218,16 @@ int dg_quantize_a_1x128(const float* x, uint8_t* q, float* sfa, int m, int k, dg
  * the last row block may be partial.
  */
 int dg_quantize_b_128x128(const float* x, uint8_t* q, float* sfb, int n, int k, dg_stream_t stream);
+
+/*
+ * FP4 quantisers: as dg_quantize_a_1x128 / dg_quantize_b_128x128 with e2m1
+ * codes (range 6): per block amax (floored at 1e-4), s = amax / 6 (fp32,
+ * correctly rounded), code = e2m1(x / s) rounded to nearest with ties to
+ * even, saturated at 6.  q is [m][k/2] (resp. [n][k/2]) bytes, two codes per
+ * byte, element 2i in the low nibble; the scale layouts are the FP8 ones.
+ */
+int dg_quantize_a_1x128_fp4(const float* x, uint8_t* q, float* sfa, int m, int k, dg_stream_t stream);
+int dg_quantize_b_128x128_fp4(const float* x, uint8_t* q, float* sfb, int n, int k, dg_stream_t stream);
 
 /*
  * Pre-allocate the split-K workspace of the current device with room for

@@ -113,6 +113,20 @@ def run_kgrouped(qa, sa, qb, sb, k_sizes, dev, guard=256):
     return d, flat
 
 
+def run_fp4(pa, sa, pb, sb, dev, guard=256):
+    """FP4 GEMM on packed e2m1 operands (uint8 [m, k/2], [n, k/2])."""
+    m = pa.shape[0]
+    n = pb.shape[0]
+    a = torch.from_numpy(np.ascontiguousarray(pa, np.uint8)).to(dev)
+    b = torch.from_numpy(np.ascontiguousarray(pb, np.uint8)).to(dev)
+    sfa = f32_to_device(slab_major(sa), dev)
+    sfb = f32_to_device(sb, dev)
+    d, flat = sentinel_bf16((m, n), dev, guard)
+    dg.fp4_gemm_nt((a, sfa), (b, sfb), d)
+    torch.cuda.synchronize()
+    return d, flat
+
+
 def run_bf16(a_bits, b_bits, dev, guard=256):
     m, k = a_bits.shape
     n = b_bits.shape[0]

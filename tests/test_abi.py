@@ -108,6 +108,20 @@ def test_bf16_validation(lib):
     assert f(GOOD, GOOD, GOOD, 0, 64, 128, None) == 0       # m = 0: no-op
 
 
+def test_fp4_validation(lib):
+    f = lib.dg_fp4_gemm_nt
+    assert f(GOOD, GOOD, GOOD, None, GOOD, 64, 64, 256, None) == 1      # null sfb
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, -1, 64, 256, None) == 1      # negative m
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, 64, 64, 128, None) == 2      # k not whole 128-byte rows
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, 64, 64, 384, None) == 2
+    assert f(GOOD, ODD, GOOD, GOOD, GOOD, 64, 64, 256, None) == 3       # misaligned sfa
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, 0, 64, 256, None) == 0       # m = 0: no-op
+    assert lib.dg_quantize_a_1x128_fp4(None, GOOD, GOOD, 4, 128, None) == 1
+    assert lib.dg_quantize_a_1x128_fp4(GOOD, GOOD, GOOD, 4, 192, None) == 2
+    assert lib.dg_quantize_b_128x128_fp4(GOOD, ODD, GOOD, 4, 128, None) == 3
+    assert lib.dg_quantize_b_128x128_fp4(GOOD, GOOD, GOOD, 0, 128, None) == 0
+
+
 def test_quant_validation(lib):
     assert lib.dg_quantize_a_1x128(None, GOOD, GOOD, 4, 128, None) == 1
     assert lib.dg_quantize_a_1x128(GOOD, GOOD, GOOD, 4, 130, None) == 2

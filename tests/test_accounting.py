@@ -35,6 +35,9 @@ def test_named_workload_sizes():
     assert b == 245395456 and f == 2.0 * 4096 * 7168 * 16384
     f, b = W.workload_work("moe_contiguous_4x8192_n4096_k7168")
     assert b == 628256768
+    f, b = W.workload_work("fp4_dense_4096x7168x16384")
+    # the FP8 large shape's bytes with A and B at half a byte per element
+    assert f == 2.0 * 4096 * 7168 * 16384 and b == 245395456 - (4096 + 7168) * 16384 // 2
     f, b = W.workload_work("moe_masked_16x256_n4096_k7168")
     assert b == 502088928 and f == 2.0 * 2067 * 4096 * 7168
     # the fused FC1 + SwiGLU on the same inputs: D (2 bytes x 4096) becomes h

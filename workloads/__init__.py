@@ -23,7 +23,7 @@ class Workload:
 
     def __init__(self, name, kind, desc, **shape):
         self.name = name
-        self.kind = kind  # "dense" | "contiguous" | "masked" | "kgrouped" | "bf16" | "swiglu"
+        self.kind = kind  # "dense" | "contiguous" | "masked" | "kgrouped" | "bf16" | "swiglu" | "fp4"
         self.desc = desc
         self.shape = shape
 
@@ -49,6 +49,10 @@ WORKLOADS = {
         "moe_masked_16x256_n4096_k7168", "masked",
         "MoE grouped masked decode, 16 experts, max_m=256, N=4096 K=7168",
         g=16, max_m=256, n=4096, k=7168, b_std=0.02),
+    # FP4 (e2m1) dense GEMM on the large dense shape, drawn as that shape
+    "fp4_dense_4096x7168x16384": Workload(
+        "fp4_dense_4096x7168x16384", "fp4", "FP4 dense GEMM (M=4096 N=7168 K=16384)",
+        m=4096, n=7168, k=16384, b_std=1.0),
     # MoE FC1 + SwiGLU + FP8 requantisation on the masked decode layout: the
     # masked shape read as [gate; up] (2I = 4096 rows, I = 2048), drawn with
     # the same seed, so its inputs equal the masked workload's
@@ -138,7 +142,7 @@ def draw(name, seed=0):
     """Draw the named workload's inputs with its recipe."""
     w = WORKLOADS[name]
     s = w.shape
-    if w.kind in ("dense", "bf16"):
+    if w.kind in ("dense", "bf16", "fp4"):
         return draw_dense(s["m"], s["n"], s["k"], seed, s["b_std"])
     if w.kind == "contiguous":
         return draw_contiguous(s["group_rows"], s["n"], s["k"], seed, s["b_std"])
@@ -187,6 +191,10 @@ def algorithmic_work(kind, **p):
         nbytes = (rows * k + 4 * rows * kb + experts * (n * k + 4 * nb * kb) + 4 * cnt.size
                   + rows * i + 4 * rows * (i // SLAB))
         return flops, nbytes
+    elif kind == "fp4":
+        # half a byte per element of A and B, their fp32 scales, bf16 D
+        m = p["m"]
+        return 2.0 * m * n * k, m * k // 2 + 4 * m * kb + n * k // 2 + 4 * nb * kb + 2 * m * n
     elif kind == "bf16":
         # two bytes per element of A, B and D; no scales
         m = p["m"]
@@ -218,8 +226,8 @@ def workload_work(name, inputs=None):
     if w.kind == "contiguous":
         mi = inputs["m_indices"] if inputs is not None else contiguous_indices(s["group_rows"])
         return algorithmic_work("contiguous", m_indices=mi, g=len(s["group_rows"]), n=s["n"], k=s["k"])
-    if w.kind == "bf16":
-        return algorithmic_work("bf16", m=s["m"], n=s["n"], k=s["k"])
+    if w.kind in ("bf16", "fp4"):
+        return algorithmic_work(w.kind, m=s["m"], n=s["n"], k=s["k"])
     if w.kind == "kgrouped":
         return algorithmic_work("kgrouped", k_sizes=s["k_sizes"], m=s["m"], n=s["n"], k=int(sum(s["k_sizes"])))
     if w.kind == "swiglu":
