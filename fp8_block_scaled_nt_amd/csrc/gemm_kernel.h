@@ -60,13 +60,13 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 // activation rule, so the second GEMM reads h as FP8 without a round trip.
 enum Epilogue { kEpiBf16 = 0, kEpiSwigluFp8 = 1 };
 
-constexpr int kSlab = 128;        // K bytes per slab (one scale per slab)
+constexpr int kSlab = 128;        // K bytes per slab (fp8: one scale slab; fp4: two)
 constexpr int kNumXcd = 8;        // MI355X: 8 XCDs, workgroups dealt round-robin
-constexpr int kDmaBytes = 1024;
+constexpr int kDmaBytes = 1024;   // LDS bytes one wave-wide 16-byte-per-lane DMA writes
 // Word 3 of a raw buffer resource for gfx9 (32-bit data format; offsets past
 // num_records read as zero) and the SC1 cache-policy bit of buffer accesses.
 constexpr int kBufferRsrcWord3 = 0x00020000;
-constexpr int kCpolSc1 = 16;   // LDS bytes one wave-wide 16-byte-per-lane DMA writes
+constexpr int kCpolSc1 = 16;
 
 struct GemmParams {
   const uint8_t* a;

@@ -44,3 +44,67 @@ def test_graph_replays_match_eager(gpu):
         # eager work between replays
         dg.fp8_gemm_nt((qa, sfa), (qb, sfb), d_eager)
         torch.cuda.synchronize()
+
+
+def _replay_check(graph, outputs, refs, eager, label):
+    for rep in range(4):
+        for o in outputs:
+            o.view(torch.uint8).fill_(0x7F)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for o, r in zip(outputs, refs):
+            assert np.array_equal(o.view(torch.uint8).cpu().numpy(), r), f"{label}: replay {rep} differs from eager"
+        eager()
+        torch.cuda.synchronize()
+
+
+def test_graph_swiglu_and_fp4(gpu):
+    """The fused FC1 + SwiGLU (masked counts read on the device) and the FP4
+    quantise + GEMM, captured together; the masked counts change between
+    replays from the host side, and each replay must match an eager run
+    with the counts it saw."""
+    rng = np.random.default_rng(77)
+    g, max_m, inter, k = 4, 96, 256, 512
+    xa = torch.from_numpy(rng.standard_normal((g, max_m, k), dtype=np.float32)).to(gpu)
+    xb = torch.from_numpy((rng.standard_normal((g, 2 * inter, k)) * 0.02).astype(np.float32)).to(gpu)
+    qa, sfa = dg.quantize_a_1x128(xa)
+    qb, sfb = dg.quantize_b_128x128(xb)
+    mm = torch.tensor([96, 0, 33, 70], dtype=torch.int32, device=gpu)
+    ld = dg.get_sfa_ld(max_m)
+    hq = torch.empty((g, max_m, inter), dtype=torch.float8_e4m3fn, device=gpu)
+    hs = torch.empty((g, inter // 128, ld), dtype=torch.float32, device=gpu)
+    x4 = torch.from_numpy(rng.standard_normal((64, 1024), dtype=np.float32)).to(gpu)
+    w4 = torch.from_numpy(rng.standard_normal((300, 1024), dtype=np.float32)).to(gpu)
+    qb4, sfb4 = dg.quantize_b_128x128_fp4(w4)
+    qa4 = torch.empty((64, 512), dtype=torch.uint8, device=gpu)
+    sfa4 = dg.empty_sfa(64, 1024, None, gpu)
+    d4 = torch.empty((64, 300), dtype=torch.bfloat16, device=gpu)
+    dg.reserve_workspace(16 << 20)
+
+    def run():
+        dg.m_grouped_fp8_gemm_nt_masked_swiglu((qa, sfa), (qb, sfb), (hq, hs), mm)
+        dg.quantize_a_1x128_fp4(x4, qa4, sfa4)
+        dg.fp4_gemm_nt((qa4, sfa4), (qb4, sfb4), d4)
+
+    def eager_refs():
+        for o in (hq, hs, d4):
+            o.view(torch.uint8).fill_(0x7F)
+        run()
+        torch.cuda.synchronize()
+        return [o.view(torch.uint8).cpu().numpy().copy() for o in (hq, hs, d4)]
+
+    refs = eager_refs()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    print("[case] graph capture of FC1 + SwiGLU and FP4 quantise + GEMM", flush=True)
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            run()
+    torch.cuda.synchronize()
+    _replay_check(graph, [hq, hs, d4], refs, run, "swiglu + fp4")
+    # new counts, written on the device between replays: the replay follows them
+    mm.copy_(torch.tensor([5, 96, 0, 64], dtype=torch.int32))
+    torch.cuda.synchronize()
+    refs = eager_refs()
+    _replay_check(graph, [hq, hs, d4], refs, run, "swiglu + fp4, new counts")
