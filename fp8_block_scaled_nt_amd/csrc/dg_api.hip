@@ -100,7 +100,7 @@ template <int BM, int BN, int WM, int WN, int NST, int VAR, int SCHED = dg::kInt
 Config make_config(const char* name) {
   return Config{name, VAR, BM, BN, WM, WN, NST, SCHED, DT, EPI,
                 reinterpret_cast<const void*>(&dg::gemm_fp8_nt_kernel<BM, BN, WM, WN, NST, VAR, SCHED, DT, EPI>),
-                dg::Smem<BM, BN, NST, DT == dg::kFp4 ? 2 : 1>::kBytes};
+                dg::Smem<BM, BN, NST, DT == dg::kFp4 ? 2 : 1, SCHED == dg::kSingleB>::kBytes};
 }
 
 const Config* configs(int* count) {
@@ -108,6 +108,7 @@ const Config* configs(int* count) {
       // dense
       make_config<256, 256, 2, 4, 2, dg::kDense>("dense_256x256_w8_s2"),
       make_config<256, 256, 2, 4, 2, dg::kDense, dg::kPingPong>("dense_256x256_w8_s2_pp"),
+      make_config<128, 256, 1, 4, 2, dg::kDense, dg::kSingleB>("dense_128x256_w4_s2_sb"),
       make_config<256, 224, 4, 2, 2, dg::kDense>("dense_256x224_w8_s2"),
       make_config<128, 256, 1, 4, 3, dg::kDense>("dense_128x256_w4_s3_wide"),
       make_config<256, 128, 4, 2, 3, dg::kDense>("dense_256x128_w8_s3"),
@@ -127,6 +128,7 @@ const Config* configs(int* count) {
       make_config<128, 128, 2, 2, 2, dg::kContiguous>("contig_128x128_w4_s2"),
       make_config<128, 256, 2, 4, 2, dg::kContiguous>("contig_128x256_w8_s2"),
       make_config<128, 256, 1, 4, 3, dg::kContiguous>("contig_128x256_w4_s3"),
+      make_config<128, 256, 1, 4, 2, dg::kContiguous, dg::kSingleB>("contig_128x256_w4_s2_sb"),
       make_config<128, 256, 1, 4, 2, dg::kContiguous>("contig_128x256_w4_s2"),
       // masked
       make_config<256, 256, 2, 4, 2, dg::kMasked>("masked_256x256_w8_s2"),
@@ -299,7 +301,7 @@ int launch_dense(const Config* c, dg::GemmParams& p, int dev, const DeviceInfo* 
   // splits of 64 x 32 tiles beat one workgroup per CU by ~15%.
   int splits = 1;
   if (const char* e = getenv("DG_SPLIT_K")) splits = atoi(e);
-  else if (c->sched == dg::kInterleaved && p.num_tiles * 2 <= info->cus && p.kb_count >= 4) {
+  else if (c->sched != dg::kPingPong && p.num_tiles * 2 <= info->cus && p.kb_count >= 4) {
     splits = 2 * info->cus / p.num_tiles - 1;
     const int min_split_slabs = 2;
     if (splits > p.kb_count / min_split_slabs) splits = p.kb_count / min_split_slabs;
@@ -312,7 +314,7 @@ int launch_dense(const Config* c, dg::GemmParams& p, int dev, const DeviceInfo* 
     p.split_slabs = per;
   }
   if (p.splits > 1) {
-    if (c->sched != dg::kInterleaved)
+    if (c->sched == dg::kPingPong)
       return fail(DG_ERR_INVALID_ARGUMENT, "configuration %s does not support split-K", c->name);
     if ((size_t)p.num_tiles > kCounterInts)
       return fail(DG_ERR_UNSUPPORTED_SHAPE, "too many tiles for split-K (%d)", p.num_tiles);
@@ -502,7 +504,12 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, cons
   if (int s = current_device(&dev, &info)) return s;
   const Config* c;
   if (int s = forced_config(dg::kContiguous, &c)) return s;
-  if (!c) c = find_config("contig_128x128_w4_s2", dg::kContiguous);
+  if (!c) {
+    // 128 x 256 tiles with one B buffer (two workgroups per CU) once there
+    // are enough of them to fill the GPU; 128 x 128 tiles below that
+    const long long tiles = (long long)(m / 128) * ((n + 255) / 256);
+    c = find_config(tiles >= info->cus ? "contig_128x256_w4_s2_sb" : "contig_128x128_w4_s2", dg::kContiguous);
+  }
   dg::GemmParams p{};
   p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.m_indices = m_indices;
   p.num_groups = num_groups;

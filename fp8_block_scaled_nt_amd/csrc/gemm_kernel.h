@@ -205,19 +205,21 @@ __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b) {
 
 // LDS layout: NST stages, each holding one slab of the A tile, of the B
 // tile, the A row scales and the B block scales of that slab (SPS scale
-// slabs per stage: 2 for FP4); the epilogue reuses the space for the bf16
-// output tile.
-template <int BM, int BN, int NST, int SPS = 1>
+// slabs per stage: 2 for FP4); with SB (single B buffer) the B tile has one
+// buffer after the stages instead of one per stage.  The epilogue reuses the
+// space for the bf16 output tile.
+template <int BM, int BN, int NST, int SPS = 1, bool SB = false>
 struct Smem {
   static constexpr int kA = BM * kSlab;
-  static constexpr int kB = BN * kSlab;
+  static constexpr int kB = SB ? 0 : BN * kSlab;  // B bytes in each stage
   static constexpr int kSa = BM * 4 * SPS;
   static constexpr int kSbCount = BN / 128 + 2;  // 128-row blocks a BN-wide tile can touch
   static constexpr int kSb = 256 * SPS;          // one dword DMA instruction's footprint per scale slab
   static constexpr int kStage = kA + kB + kSa + kSb;
+  static constexpr int kBShared = NST * kStage;  // SB: offset of the one B buffer
   static constexpr int kOutPitch = BN * 2 + 16;  // bf16 output row pitch (bytes)
   static constexpr int kOut = BM * kOutPitch;
-  static constexpr int kMain = NST * kStage;
+  static constexpr int kMain = NST * kStage + (SB ? BN * kSlab : 0);
   static constexpr int kBytes = kMain > kOut ? kMain : kOut;
 };
 
@@ -252,9 +254,13 @@ __device__ __forceinline__ int loads_ahead(int kb, int KB) {
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 // SCHED selects the main-loop schedule: kInterleaved (every wave loads and
-// computes each slab; one barrier per slab) or kPingPong (8 waves in two
-// groups that alternate load and compute steps, see below).
-enum Schedule { kInterleaved = 0, kPingPong = 1 };
+// computes each slab; one barrier per slab), kPingPong (8 waves in two
+// groups that alternate load and compute steps, see below) or kSingleB (the
+// interleaved loop with one B buffer: every wave reads its B fragments of a
+// slab into registers first, and the next slab's B is loaded over them after
+// a second barrier; the smaller LDS footprint fits two workgroups per CU,
+// whose phases then overlap).
+enum Schedule { kInterleaved = 0, kPingPong = 1, kSingleB = 2 };
 
 template <int BM, int BN, int WM, int WN, int NST, int VAR, int SCHED = kInterleaved, int DT = kFp8,
           int EPI = kEpiBf16>
@@ -266,7 +272,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   constexpr int kJa = BM / 8;  // DMA instructions per slab for A (1 KiB each)
   constexpr int kJb = BN / 8;
   constexpr int kSps = DT == kFp4 ? 2 : 1;  // scale slabs per 128-byte slab
-  using S = Smem<BM, BN, NST, kSps>;
+  constexpr bool kSB = SCHED == kSingleB;
+  using S = Smem<BM, BN, NST, kSps, kSB>;
+  static_assert(!kSB || NST == 2, "one B buffer: the next slab's B lands while this one is computed");
   static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be whole fragments");
   static_assert(BM <= kThreads, "row-tag pass needs one thread per tile row");
   static_assert(NST >= 2, "pipeline shape");
@@ -275,7 +283,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   // its last TN / 2 the matching up rows, so gate and up meet in one lane.
   static_assert(EPI == kEpiBf16 || (VAR == kMasked && DT == kFp8 && BN == 256 && TN % 32 == 0),
                 "SwiGLU epilogue shape");
-  static_assert(DT != kFp4 || (VAR == kDense && SCHED == kInterleaved && EPI == kEpiBf16),
+  static_assert(DT != kFp4 || (VAR == kDense && SCHED != kPingPong && EPI == kEpiBf16),
                 "the FP4 path is the dense interleaved GEMM");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -453,7 +461,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
       const int jj = d - kPerWaveA;
       const int j = jj * kWaves + wave;
       if (kJb % kWaves != 0 && j >= kJb) return;
-      lds_dma16(rs_b, b_off[jj], (uint32_t)kb * kSlab, st + S::kA + j * kDmaBytes);
+      lds_dma16(rs_b, b_off[jj], (uint32_t)kb * kSlab, (kSB ? smem + S::kBShared : st + S::kA) + j * kDmaBytes);
     } else {
       const int e = d - kPerWaveA - kPerWaveB;
       const int h = e >> 1;                 // scale slab of this slab
@@ -661,12 +669,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
       wait_vmem_dyn(c_loads * loads_ahead<NST>(kb, KB));
       block_barrier();  // also: every wave is done with the stage about to be refilled
       __builtin_amdgcn_sched_barrier(0);
-      if (kb + NST - 1 < KB) issue_slab(kb + NST - 1, (kb + NST - 1) % NST);
+      if (!kSB && kb + NST - 1 < KB) issue_slab(kb + NST - 1, (kb + NST - 1) % NST);
       __builtin_amdgcn_sched_barrier(0);
 
       const uint8_t* st = smem + (kb % NST) * S::kStage;
       const uint8_t* sA = st;
-      const uint8_t* sB = st + S::kA;
+      const uint8_t* sB = kSB ? smem + S::kBShared : st + S::kA;
       const float* sSa = (const float*)(st + S::kA + S::kB);
       const float* sSb = (const float*)(st + S::kA + S::kB + S::kSa);
 
@@ -681,6 +689,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
         const v4i lo = *(const v4i*)(sB + f * 2048 + frag_lo);
         const v4i hi = *(const v4i*)(sB + f * 2048 + frag_hi);
         bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      if constexpr (kSB) {
+        // every wave holds its B fragments of slab kb: the B buffer is free
+        // for slab kb + 1 (and the other A stage since the first barrier)
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's B reads are done
+        block_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (kb + 1 < KB) issue_slab(kb + 1, (kb + 1) % NST);
+        __builtin_amdgcn_sched_barrier(0);
       }
 
       // Software pipeline over the wave's FM x FN fragments (row-major order t):
@@ -898,7 +915,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   // which are coherent across the per-XCD L2s (the agent-scope path), so no
   // L2 write-back or invalidate is needed.  The reducer reads kChunk splits'
   // partials per batch; loads past the last split return zero.
-  if constexpr (VAR == kDense && SCHED == kInterleaved) if (p.splits > 1) {
+  if constexpr (VAR == kDense && SCHED != kPingPong) if (p.splits > 1) {
     constexpr int kTileFloats = BM * BN;
     constexpr int kChunk = (FM * FN * 4) >= 128 ? 1 : 128 / (FM * FN * 4);
     float* part = p.ws_partial + (size_t)tile_id * p.splits * kTileFloats;

@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 DENSE_CONFIGS = ["dense_256x256_w8_s2", "dense_256x128_w8_s3", "dense_128x256_w8_s3", "dense_128x128_w4_s3",
                  "dense_128x128_w4_s2", "dense_64x64_w4_s3", "dense_64x64_w4_s8", "dense_64x32_w4_s4", "dense_256x224_w8_s2",
                  "dense_128x256_w4_s3_wide", "dense_256x256_w8_s2_pp", "dense_256x128_w4_s2",
-                 "dense_256x128_w4_s3", "dense_128x256_w4_s3"]
+                 "dense_256x128_w4_s3", "dense_128x256_w4_s3", "dense_128x256_w4_s2_sb"]
 
 
 def dense_case(m, n, k, seed, b_std=1.0):
@@ -83,7 +83,8 @@ def test_dense_unit_scale_exact_values(gpu):
 
 
 @pytest.mark.parametrize("cfg", [None, "contig_128x256_w8_s3", "contig_128x128_w4_s3", "contig_128x128_w4_s2",
-                                 "contig_128x256_w8_s2", "contig_128x256_w4_s3", "contig_128x256_w4_s2"])
+                                 "contig_128x256_w8_s2", "contig_128x256_w4_s3", "contig_128x256_w4_s2",
+                                 "contig_128x256_w4_s2_sb"])
 def test_contiguous(gpu, cfg, monkeypatch):
     if cfg:
         monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
