@@ -26,6 +26,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -62,11 +63,17 @@ def parse():
 
 
 def source_hash():
+    """Hash of the kernel sources with comments and blank space removed, so
+    that an edit of comments alone keeps the recorded counters valid."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp8_block_scaled_nt_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        text = " ".join(text.split())
+        h.update(f.encode() + text.encode())
     return h.hexdigest()[:16]
 
 

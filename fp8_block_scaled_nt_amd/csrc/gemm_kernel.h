@@ -13,8 +13,9 @@
 //  * promotion: acc += p * (sa[row] * sb[col block]) in fp32 VGPRs after each
 //    slab (the MFMA's own E8M0 scales stay neutral: the fp32 block scales
 //    are not powers of two);
-//  * operand tiles move HBM/L2 -> LDS with global_load_lds_dwordx4 (no VGPR
-//    staging), NST-stage buffered, one workgroup barrier per slab;
+//  * operand tiles move HBM/L2 -> LDS with LDS DMA (buffer_load_dwordx4 ...
+//    lds, no VGPR staging), NST-stage buffered, one workgroup barrier per
+//    slab (the schedules below vary this);
 //  * each DMA instruction reads 8 whole 128-byte rows (8 lanes per cache
 //    line): on gfx950 this moves ~3.7x more bytes per clock into a CU than
 //    instructions that cover 16 half lines.  LDS keeps the tile row-major,
@@ -29,7 +30,10 @@
 // holds 32 K-bytes of row (l % 16); any K order works as long as A and B use
 // the same one.  Here lane l holds K bytes [16*(l/16), +16) in its low four
 // VGPRs and [64 + 16*(l/16), +16) in its high four.  The fp32 result lane l,
-// element i is row 4*(l/16) + i, column l % 16 of the 16x16 fragment.
+// element i is row 4*(l/16) + i, column l % 16 of the 16x16 fragment.  The
+// same kernel also runs bf16 operands (no scales) and e2m1 operands (FP4,
+// block scales), and a SwiGLU + FP8 requantisation epilogue on the masked
+// layout.
 #pragma once
 
 #include <hip/hip_runtime.h>
