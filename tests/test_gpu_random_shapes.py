@@ -109,3 +109,38 @@ def test_random_grouped(gpu, case):
     assert res["ok"], res
     assert np.all(H.d_bits(d)[~valid] == H.SENTINEL)
     assert H.guard_untouched(flat, d.numel())
+
+
+@pytest.mark.parametrize("case", range(4))
+def test_random_k_grouped(gpu, case):
+    rng = np.random.default_rng(RNG_SEED + 200 + case)
+    g = int(rng.integers(1, 5))
+    m = int(rng.integers(1, 400))
+    n = int(rng.integers(1, 400))
+    sizes = [128 * int(v) for v in rng.integers(0, 4, g)]
+    x = W.draw_kgrouped(sizes, m, n, seed=case, k_total=max(sum(sizes), 128))
+    qa, sa = oracle.quantize_a_1x128(x["a"])
+    qb, sb = oracle.quantize_b_128x128(x["b"])
+    print(f"[case] random k-grouped m={m} n={n} sizes={sizes}", flush=True)
+    d, flat = H.run_kgrouped(qa, sa, qb, sb, sizes, gpu)
+    r = oracle.k_grouped_ref(qa, sa, qb, sb, sizes)
+    res = oracle.tolerance_check(H.d_float(d), r)
+    assert res["ok"], res
+    assert H.guard_untouched(flat, d.numel())
+
+
+@pytest.mark.parametrize("case", range(4))
+def test_random_swiglu(gpu, case):
+    from tests import test_gpu_swiglu as SW
+    rng = np.random.default_rng(RNG_SEED + 300 + case)
+    g = int(rng.integers(1, 5))
+    max_m = int(rng.integers(1, 300))
+    inter = 128 * int(rng.integers(1, 4))
+    k = 128 * int(rng.integers(1, 5))
+    mm = rng.integers(-1, max_m + 20, g).astype(np.int32)
+    qa, sa, qb, sb, mm = SW.workload_case(g, max_m, inter, k, mm, seed=case)
+    print(f"[case] random swiglu g={g} max_m={max_m} I={inter} k={k} counts={mm.tolist()}", flush=True)
+    hq, hs, fq, fs = H.run_swiglu(qa, sa, qb, sb, mm, gpu)
+    assert H.swiglu_guards_untouched(fq, fs, hq.size, hs.size)
+    code_share, _ = SW.check_call(hq, hs, qa, sa, qb, sb, mm, SW.rule_tol, f"random swiglu {case}", 0.1)
+    assert code_share >= 0.98, code_share

@@ -163,8 +163,10 @@ def check_call(hq, hs_bits, qa, sa, qb, sb, masked_m, tol_fn, label, min_fixed):
         fixed, total = fixed + f, total + t
         same_code.append(np.sum(T[hq[e, :cnt]] == T[hq_o[e, :cnt]]))
         same_scale.append(np.sum(s_bits.view(np.float32) == hs_o[e, :cnt]))
+    if total == 0:  # no valid row anywhere: only the sentinels were checked
+        return 1.0, 1.0
     n_scales = total // 128
-    share, code_share = fixed / max(total, 1), sum(same_code) / max(total, 1)
+    share, code_share = fixed / total, sum(same_code) / total
     scale_share = sum(same_scale) / max(n_scales, 1)
     print(f"  fixed {share:.5f} same code as the oracle {code_share:.5f} same scale {scale_share:.5f}", flush=True)
     assert share >= min_fixed, (label, share)
