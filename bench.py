@@ -104,7 +104,7 @@ class Rotation:
         return self.sets[i % self.r]
 
 
-def kernel_time_us(torch, dg, launch, rot, n_launch, warm=5):
+def kernel_time_us(torch, dg, launch, rot, n_launch, warm=20):
     """Average duration of the GEMM kernel itself over n_launch launches."""
     for i in range(warm):
         launch(rot[i])
