@@ -300,7 +300,7 @@ def cpu_oracle_baseline(np, W, inp, m, n, k, seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         return 2
     import numpy as np
