@@ -23,9 +23,12 @@
  *   torch CUDA tensor) on the current device.  The library never frees,
  *   keeps or allocates anything on behalf of a call's arguments.
  * - Every compute call is asynchronous on `stream` (0 = the null stream),
- *   performs no host<->device copy, no synchronisation and no device memory
- *   allocation, and reads no device value on the host.  The calls are
- *   therefore capturable into a HIP graph.
+ *   performs no host<->device copy and no synchronisation, and reads no
+ *   device value on the host.  The one device allocation is the split-K
+ *   workspace of the dense calls (fp8, bf16, fp4), made or grown by the first
+ *   call on a device that needs it; dg_reserve_workspace makes it ahead of
+ *   time.  Apart from that first growth the calls are capturable into a HIP
+ *   graph.
  * - Layouts are packed and row-major:
  *     A       [m][k]               (masked: [num_groups][max_m][k])
  *     B       [n][k]               (grouped: [num_groups][n][k])
@@ -34,7 +37,8 @@
  *             (masked: [num_groups][k/128][dg_get_sfa_ld(max_m)])
  *     sfb     [ceil(n/128)][k/128] (grouped: [num_groups][ceil(n/128)][k/128])
  * - Preconditions checked on the host: non-null pointers, A/B/D/sfa/sfb
- *   16-byte aligned, k >= 128 and k % 128 == 0, n >= 1, m >= 0.  m == 0 (or
+ *   16-byte aligned, k >= 128 and k % 128 == 0 (the bf16 and fp4 entry points
+ *   state their own K rule), n >= 1, m >= 0.  m == 0 (or
  *   num_groups == 0 rows) is a successful no-op.  On a failed check nothing
  *   is enqueued, D is untouched and a status other than DG_OK is returned;
  *   dg_last_error_message() then describes the failure.
