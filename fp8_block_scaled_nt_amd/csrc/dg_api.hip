@@ -306,6 +306,11 @@ int launch_dense(const Config* c, dg::GemmParams& p, int dev, const DeviceInfo* 
   if (const char* e = getenv("DG_SPLIT_K")) splits = atoi(e);
   else if (c->sched != dg::kPingPong && p.num_tiles * 2 <= info->cus && p.kb_count >= 4) {
     splits = 2 * info->cus / p.num_tiles - 1;
+    // one more split when it still fits two workgroups per CU and shortens the
+    // longest split (64 x 2112 x 7168: 7 splits of 8 slabs, 1 % ahead of 6 of 10)
+    if (p.num_tiles * (splits + 1) <= 2 * info->cus &&
+        (p.kb_count + splits) / (splits + 1) < (p.kb_count + splits - 1) / splits)
+      ++splits;
     const int min_split_slabs = 2;
     if (splits > p.kb_count / min_split_slabs) splits = p.kb_count / min_split_slabs;
     if (splits > 8) splits = 8;  // the reducer reads up to 8 partials per batch
