@@ -140,12 +140,12 @@ const Config* configs(int* count) {
       // K-grouped
       make_config<256, 256, 2, 4, 2, dg::kKGrouped>("kgrouped_256x256_w8_s2"),
       make_config<128, 128, 2, 2, 2, dg::kKGrouped>("kgrouped_128x128_w4_s2"),
-      // BF16 dense (the variant tag is kBf16Dense so that DG_FORCE_CONFIG
-      // names pick among these only)
+      // BF16 dense (find_config matches the dtype too, so DG_FORCE_CONFIG
+      // names pick among these only for the bf16 entry point)
       make_config<256, 256, 2, 4, 2, dg::kDense, dg::kInterleaved, dg::kBf16>("bf16_256x256_w8_s2"),
       make_config<128, 128, 2, 2, 2, dg::kDense, dg::kInterleaved, dg::kBf16>("bf16_128x128_w4_s2"),
       make_config<64, 32, 2, 2, 4, dg::kDense, dg::kInterleaved, dg::kBf16>("bf16_64x32_w4_s4"),
-      // FP4 (e2m1) dense
+      // FP4 (e2m1) dense (selected the same way by dtype)
       make_config<256, 256, 2, 4, 2, dg::kDense, dg::kInterleaved, dg::kFp4>("fp4_256x256_w8_s2"),
       make_config<128, 128, 2, 2, 2, dg::kDense, dg::kInterleaved, dg::kFp4>("fp4_128x128_w4_s2"),
       make_config<64, 32, 2, 2, 4, dg::kDense, dg::kInterleaved, dg::kFp4>("fp4_64x32_w4_s4"),
