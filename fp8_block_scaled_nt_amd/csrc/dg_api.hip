@@ -186,14 +186,41 @@ int forced_config(int variant, const Config** out, int dtype = dg::kFp8, int epi
 
 std::once_flag g_attr_once;
 hipError_t g_attr_err = hipSuccess;
+constexpr int kMaxConfigs = 64;
+int g_per_cu[kMaxConfigs];  // resident workgroups per CU of each configuration (0: not known)
 
 void set_kernel_attributes() {
   int cnt = 0;
   const Config* t = configs(&cnt);
   for (int i = 0; i < cnt; ++i) {
     hipError_t e = hipFuncSetAttribute(t[i].fn, hipFuncAttributeMaxDynamicSharedMemorySize, t[i].smem);
-    if (e != hipSuccess) g_attr_err = e;
+    if (e != hipSuccess) {
+      g_attr_err = e;
+      continue;
+    }
+    int blocks = 0;
+    if (i < kMaxConfigs &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, t[i].fn, t[i].threads(), t[i].smem) == hipSuccess)
+      g_per_cu[i] = blocks;
+    else
+      (void)hipGetLastError();
   }
+}
+
+int ensure_kernel_attributes() {
+  std::call_once(g_attr_once, set_kernel_attributes);
+  if (g_attr_err != hipSuccess)
+    return fail(DG_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(g_attr_err));
+  return DG_OK;
+}
+
+// Workgroups of configuration c that one CU holds at once (LDS, registers and
+// waves permitting); 1 when the runtime could not say.
+int per_cu(const Config* c) {
+  int cnt = 0;
+  const Config* t = configs(&cnt);
+  const long i = c - t;
+  return (i >= 0 && i < kMaxConfigs && g_per_cu[i] > 0) ? g_per_cu[i] : 1;
 }
 
 // ---- split-K workspace: library-owned device memory per device, grown on
@@ -233,12 +260,10 @@ int ensure_workspace(int dev, size_t partial_bytes, float** partial, int** count
 }
 
 int launch(const Config& c, dg::GemmParams& p, int grid, hipStream_t stream) {
-  std::call_once(g_attr_once, set_kernel_attributes);
-  if (g_attr_err != hipSuccess)
-    return fail(DG_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(g_attr_err));
+  if (int s = ensure_kernel_attributes()) return s;
   if (log_enabled())
-    fprintf(stderr, "[dg] %s m=%d n=%d k=%d groups=%d grid=%d threads=%d smem=%d\n", c.name, p.m, p.n,
-            p.k, p.num_groups, grid, c.threads(), c.smem);
+    fprintf(stderr, "[dg] %s m=%d n=%d k=%d groups=%d grid=%d threads=%d smem=%d per_cu=%d splits=%d\n", c.name,
+            p.m, p.n, p.k, p.num_groups, grid, c.threads(), c.smem, per_cu(&c), p.splits);
   if (grid <= 0) return ok();
   void* args[] = {&p};
   hipError_t e;
@@ -286,34 +311,46 @@ int check_rows(long long rows, int k) {
   return DG_OK;
 }
 
+// The 256 x 256 tile (one workgroup per CU) while its tiles alone keep more
+// than half the CUs busy, so that it needs no split-K; below that, 128 x 128
+// tiles (two per CU, split over K when still too few) finish sooner.  The
+// N- and M-shards of the large GEMM over 8 GPUs, 4096 x 896 x 16384 and
+// 512 x 7168 x 16384, run in 83-90 us against 107 us for 256 x 256 tiles
+// split 4 ways; 2048 x 7168 x 16384 (224 big tiles) keeps 256 x 256 tiles,
+// 258 against 288 us.
+bool big_tiles_enough(int m, int n, const DeviceInfo* info) {
+  return 2 * (long long)((m + 255) / 256) * ((n + 255) / 256) > info->cus;
+}
+
 // Dense launch with the split-K choice, shared by the fp8, bf16 and fp4 entry
 // points; k_bytes is K in bytes (one per fp8 value, two per bf16 value, half
 // per fp4 value) and scale_slabs the number of 128-wide scale slabs of K.
 int launch_dense(const Config* c, dg::GemmParams& p, int dev, const DeviceInfo* info, int m, int n, int k_bytes,
                  int scale_slabs, dg_stream_t stream) {
+  if (int s = ensure_kernel_attributes()) return s;
   p.num_groups = 1;
   fill_common(p, *c, m, n, k_bytes);
   p.sk_count = scale_slabs;
   p.num_tiles = p.tiles_m * p.tiles_n;
   p.splits = 1;
   p.split_slabs = p.kb_count;
-  // Split K over workgroups when the tiles alone cannot fill the GPU (skinny
-  // M).  Decode-shaped calls are bound by HBM latency more than by bandwidth,
-  // so about two workgroups per CU (every small-tile configuration fits two)
-  // keep more loads in flight than one; measured on 64 x 2112 x 7168, six
-  // splits of 64 x 32 tiles beat one workgroup per CU by ~15%.
+  // Split K over workgroups when the tiles alone cannot fill the GPU's
+  // workgroup slots: up to two resident workgroups per CU (one for the
+  // configurations that fit only one).  Decode-shaped calls are bound by HBM
+  // latency more than by bandwidth, and two workgroups per CU keep more loads
+  // in flight than one (64 x 2112 x 7168: 7 splits of 8 slabs of 64 x 32
+  // tiles, 462 workgroups); mid-sized shapes with too few tiles gain the same
+  // way (4096 x 896 x 16384 in 128 x 128 tiles: 2 splits, 83 against 115 us).
   int splits = 1;
+  const int slots = (per_cu(c) >= 2 ? 2 : 1) * info->cus;
   if (const char* e = getenv("DG_SPLIT_K")) splits = atoi(e);
-  else if (c->sched != dg::kPingPong && p.num_tiles * 2 <= info->cus && p.kb_count >= 4) {
-    splits = 2 * info->cus / p.num_tiles - 1;
-    // one more split when it still fits two workgroups per CU and shortens the
-    // longest split (64 x 2112 x 7168: 7 splits of 8 slabs, 1 % ahead of 6 of 10)
-    if (p.num_tiles * (splits + 1) <= 2 * info->cus &&
-        (p.kb_count + splits) / (splits + 1) < (p.kb_count + splits - 1) / splits)
-      ++splits;
+  else if (c->sched != dg::kPingPong && p.num_tiles * 2 <= slots && p.kb_count >= 4) {
+    splits = slots / p.num_tiles;
+    // no more splits than it takes to shorten the longest one
+    while (splits > 1 && (p.kb_count + splits - 2) / (splits - 1) == (p.kb_count + splits - 1) / splits) --splits;
     const int min_split_slabs = 2;
     if (splits > p.kb_count / min_split_slabs) splits = p.kb_count / min_split_slabs;
-    if (splits > 8) splits = 8;  // the reducer reads up to 8 partials per batch
+    if (splits > 8) splits = 8;  // partial-tile traffic grows with the count
   }
   if (splits > 1) {
     const int per = (p.kb_count + splits - 1) / splits;
@@ -430,7 +467,8 @@ int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const f
   if (int s = forced_config(dg::kDense, &c)) return s;
   if (!c) {
     if (m <= 64) c = find_config(n <= 4096 ? "dense_64x32_w4_s4" : "dense_64x64_w4_s3", dg::kDense);
-    else if (m <= 256 || n <= 256) c = find_config("dense_128x128_w4_s2", dg::kDense);
+    else if (m <= 256 || n <= 256 || !big_tiles_enough(m, n, info))
+      c = find_config("dense_128x128_w4_s2", dg::kDense);
     else c = find_config("dense_256x256_w8_s2", dg::kDense);
   }
   dg::GemmParams p{};
@@ -455,7 +493,8 @@ int dg_bf16_gemm_nt(const uint16_t* a, const uint16_t* b, uint16_t* d, int m, in
   if (int s = forced_config(dg::kDense, &c, dg::kBf16)) return s;
   if (!c) {
     if (m <= 64) c = find_config("bf16_64x32_w4_s4", dg::kDense, dg::kBf16);
-    else if (m <= 256 || n <= 256) c = find_config("bf16_128x128_w4_s2", dg::kDense, dg::kBf16);
+    else if (m <= 256 || n <= 256 || !big_tiles_enough(m, n, info))
+      c = find_config("bf16_128x128_w4_s2", dg::kDense, dg::kBf16);
     else c = find_config("bf16_256x256_w8_s2", dg::kDense, dg::kBf16);
   }
   dg::GemmParams p{};
@@ -484,7 +523,8 @@ int dg_fp4_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const f
   if (int s = forced_config(dg::kDense, &c, dg::kFp4)) return s;
   if (!c) {
     if (m <= 64) c = find_config("fp4_64x32_w4_s4", dg::kDense, dg::kFp4);
-    else if (m <= 256 || n <= 256) c = find_config("fp4_128x128_w4_s2", dg::kDense, dg::kFp4);
+    else if (m <= 256 || n <= 256 || !big_tiles_enough(m, n, info))
+      c = find_config("fp4_128x128_w4_s2", dg::kDense, dg::kFp4);
     else c = find_config("fp4_256x256_w8_s2", dg::kDense, dg::kFp4);
   }
   dg::GemmParams p{};

@@ -161,7 +161,8 @@ def test_dense_long_k_pipeline(gpu):
     (64, 130, 896, "7"),      # one slab per split
     (100, 192, 768, "2"),     # two tile rows
 ])
-@pytest.mark.parametrize("cfg", ["dense_64x64_w4_s8", "dense_64x32_w4_s4"])
+@pytest.mark.parametrize("cfg", ["dense_64x64_w4_s8", "dense_64x32_w4_s4", "dense_128x128_w4_s2",
+                                 "dense_128x256_w4_s2_sb"])
 def test_dense_split_k(gpu, m, n, k, splits, cfg, monkeypatch):
     if splits:
         monkeypatch.setenv("DG_SPLIT_K", splits)
@@ -173,7 +174,21 @@ def test_dense_split_k(gpu, m, n, k, splits, cfg, monkeypatch):
     assert np.array_equal(H.d_bits(d), H.d_bits(d2))
 
 
-@pytest.mark.parametrize("cfg", ["dense_64x64_w4_s8", "dense_64x32_w4_s4"])
+@pytest.mark.parametrize("m,n,k", [
+    (1024, 896, 2048),   # 16 big tiles: 128 x 128 tiles, 8 splits of 2 slabs
+    (512, 1792, 1536),   # 56 tiles of 128 x 128 over 6 splits
+    (2304, 2304, 512),   # 81 big tiles: 128 x 128, no split (324 tiles, 2 slabs each)
+])
+def test_dense_default_mid_shapes(gpu, m, n, k):
+    # shapes whose 256 x 256 tiles would leave most CUs idle take the
+    # 128 x 128 tiles and, where still too few, split-K
+    qa, sa, qb, sb = dense_case(m, n, k, seed=m + n + k)
+    d = check_dense(gpu, qa, sa, qb, sb, label=f"default mid shape {m}x{n}x{k}")
+    d2, _ = H.run_dense(qa, sa, qb, sb, gpu)
+    assert np.array_equal(H.d_bits(d), H.d_bits(d2))
+
+
+@pytest.mark.parametrize("cfg", ["dense_64x64_w4_s8", "dense_64x32_w4_s4", "dense_128x128_w4_s2"])
 def test_split_k_back_to_back_shapes(gpu, cfg, monkeypatch):
     # calls with different split counts and tile counts in a row share the workspace
     monkeypatch.setenv("DG_FORCE_CONFIG", cfg)

@@ -102,6 +102,14 @@ def test_dense_large_full(gpu):
     dense_case(gpu, "dense_large_4096x7168x16384")
 
 
+def test_dense_shard_n_full(gpu):
+    dense_case(gpu, "dense_shard_n_4096x896x16384")
+
+
+def test_dense_shard_m_full(gpu):
+    dense_case(gpu, "dense_shard_m_512x7168x16384")
+
+
 def test_contiguous_full(gpu):
     name = "moe_contiguous_4x8192_n4096_k7168"
     w = W.WORKLOADS[name]

@@ -41,6 +41,15 @@ WORKLOADS = {
     "dense_large_4096x7168x16384": Workload(
         "dense_large_4096x7168x16384", "dense", "dense large GEMM (M=4096 N=7168 K=16384)",
         m=4096, n=7168, k=16384, b_std=1.0),
+    # One GPU's share of the large GEMM sharded over 8 GPUs: split N (each
+    # GPU holds 896 of B's 7168 rows) or split M (512 of A's 4096 rows),
+    # drawn like the large shape
+    "dense_shard_n_4096x896x16384": Workload(
+        "dense_shard_n_4096x896x16384", "dense", "dense large GEMM, N/8 shard (M=4096 N=896 K=16384)",
+        m=4096, n=896, k=16384, b_std=1.0),
+    "dense_shard_m_512x7168x16384": Workload(
+        "dense_shard_m_512x7168x16384", "dense", "dense large GEMM, M/8 shard (M=512 N=7168 K=16384)",
+        m=512, n=7168, k=16384, b_std=1.0),
     "moe_contiguous_4x8192_n4096_k7168": Workload(
         "moe_contiguous_4x8192_n4096_k7168", "contiguous",
         "MoE grouped contiguous, 4 experts x 8192 rows, N=4096 K=7168",
