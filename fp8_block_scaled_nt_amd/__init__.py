@@ -30,7 +30,7 @@ __all__ = [
     "m_grouped_fp8_gemm_nt_masked", "m_grouped_fp8_gemm_nt_masked_swiglu", "quantize_a_1x128", "quantize_b_128x128",
     "k_grouped_fp8_gemm_nt", "bf16_gemm_nt", "fp4_gemm_nt", "quantize_a_1x128_fp4", "quantize_b_128x128_fp4", "get_m_alignment_for_contiguous_layout", "get_sfa_ld", "empty_sfa",
     "profile_next_launch",
-    "reserve_workspace",
+    "reserve_workspace", "dense_workspace_size",
 ]
 
 
@@ -63,6 +63,7 @@ _SIGNATURES = {
     "dg_version": [],
     "dg_profile_next_launch": [_vp, _vp],
     "dg_reserve_workspace": [ctypes.c_size_t],
+    "dg_dense_workspace_size": [_ci, _ci, _ci, _ci, ctypes.POINTER(ctypes.c_size_t)],
 }
 _RESTYPES = {"dg_status_string": ctypes.c_char_p, "dg_last_error_message": ctypes.c_char_p,
              "dg_version": ctypes.c_char_p}
@@ -123,6 +124,20 @@ def profile_next_launch(start_event, stop_event):
 def reserve_workspace(nbytes):
     """Pre-allocate the split-K workspace on the current device."""
     _check(lib().dg_reserve_workspace(int(nbytes)))
+
+
+_DTYPES = {"fp8": 0, "bf16": 1, "fp4": 2}
+
+
+def dense_workspace_size(m, n, k, dtype="fp8"):
+    """Split-K workspace bytes a dense call (fp8_gemm_nt, bf16_gemm_nt or
+    fp4_gemm_nt) of this shape makes on the current device; 0 if it does not
+    split K.  Give it to reserve_workspace before capturing such calls."""
+    if dtype not in _DTYPES:
+        raise ValueError(f"dtype must be one of {sorted(_DTYPES)}")
+    out = ctypes.c_size_t(0)
+    _check(lib().dg_dense_workspace_size(_DTYPES[dtype], int(m), int(n), int(k), ctypes.byref(out)))
+    return out.value
 
 
 def get_m_alignment_for_contiguous_layout():

@@ -322,6 +322,62 @@ bool big_tiles_enough(int m, int n, const DeviceInfo* info) {
   return 2 * (long long)((m + 255) / 256) * ((n + 255) / 256) > info->cus;
 }
 
+// Split count of a dense launch of num_tiles tiles over kb_count 128-byte K
+// slabs (1: no split), and the slabs of each split.
+//
+// K is split over workgroups when the tiles alone cannot fill the GPU's
+// workgroup slots: up to two resident workgroups per CU (one for the
+// configurations that fit only one).  Decode-shaped calls are bound by HBM
+// latency more than by bandwidth, and two workgroups per CU keep more loads
+// in flight than one (64 x 2112 x 7168: 7 splits of 8 slabs of 64 x 32 tiles,
+// 462 workgroups); mid-sized shapes with too few tiles gain the same way
+// (4096 x 896 x 16384 in 128 x 128 tiles: 2 splits, 83 against 115 us).
+// DG_SPLIT_K=<n> pins the count (for sweeps).
+int dense_splits(const Config* c, int num_tiles, int kb_count, const DeviceInfo* info, int* split_slabs) {
+  int splits = 1;
+  const int slots = (per_cu(c) >= 2 ? 2 : 1) * info->cus;
+  if (const char* e = getenv("DG_SPLIT_K")) splits = atoi(e);
+  else if (c->sched != dg::kPingPong && num_tiles * 2 <= slots && kb_count >= 4) {
+    splits = slots / num_tiles;
+    // no more splits than it takes to shorten the longest one
+    while (splits > 1 && (kb_count + splits - 2) / (splits - 1) == (kb_count + splits - 1) / splits) --splits;
+    const int min_split_slabs = 2;
+    if (splits > kb_count / min_split_slabs) splits = kb_count / min_split_slabs;
+    if (splits > 8) splits = 8;  // partial-tile traffic grows with the count
+  }
+  *split_slabs = kb_count;
+  if (splits <= 1) return 1;
+  const int per = (kb_count + splits - 1) / splits;
+  *split_slabs = per;
+  return (kb_count + per - 1) / per;  // no empty splits
+}
+
+// The default configuration of a dense call (the rules and their
+// measurements are next to big_tiles_enough and in the config table).
+const Config* dense_default_config(int dtype, int m, int n, const DeviceInfo* info) {
+  const bool mid = m <= 256 || n <= 256 || !big_tiles_enough(m, n, info);
+  switch (dtype) {
+    case dg::kBf16:
+      if (m <= 64) return find_config("bf16_64x32_w4_s4", dg::kDense, dg::kBf16);
+      return find_config(mid ? "bf16_128x128_w4_s2" : "bf16_256x256_w8_s2", dg::kDense, dg::kBf16);
+    case dg::kFp4:
+      if (m <= 64) return find_config("fp4_64x32_w4_s4", dg::kDense, dg::kFp4);
+      return find_config(mid ? "fp4_128x128_w4_s2" : "fp4_256x256_w8_s2", dg::kDense, dg::kFp4);
+    default:
+      if (m <= 64) return find_config(n <= 4096 ? "dense_64x32_w4_s4" : "dense_64x64_w4_s3", dg::kDense);
+      return find_config(mid ? "dense_128x128_w4_s2" : "dense_256x256_w8_s2", dg::kDense);
+  }
+}
+
+// The configuration a dense call uses: DG_FORCE_CONFIG when it names one of
+// this dtype's dense configurations, else the default.
+int dense_config(int dtype, int m, int n, const DeviceInfo* info, const Config** out) {
+  if (int s = forced_config(dg::kDense, out, dtype)) return s;
+  if (!*out) *out = dense_default_config(dtype, m, n, info);
+  if (!*out) return fail(DG_ERR_INTERNAL, "no dense configuration for dtype %d", dtype);
+  return DG_OK;
+}
+
 // Dense launch with the split-K choice, shared by the fp8, bf16 and fp4 entry
 // points; k_bytes is K in bytes (one per fp8 value, two per bf16 value, half
 // per fp4 value) and scale_slabs the number of 128-wide scale slabs of K.
@@ -332,32 +388,7 @@ int launch_dense(const Config* c, dg::GemmParams& p, int dev, const DeviceInfo* 
   fill_common(p, *c, m, n, k_bytes);
   p.sk_count = scale_slabs;
   p.num_tiles = p.tiles_m * p.tiles_n;
-  p.splits = 1;
-  p.split_slabs = p.kb_count;
-  // Split K over workgroups when the tiles alone cannot fill the GPU's
-  // workgroup slots: up to two resident workgroups per CU (one for the
-  // configurations that fit only one).  Decode-shaped calls are bound by HBM
-  // latency more than by bandwidth, and two workgroups per CU keep more loads
-  // in flight than one (64 x 2112 x 7168: 7 splits of 8 slabs of 64 x 32
-  // tiles, 462 workgroups); mid-sized shapes with too few tiles gain the same
-  // way (4096 x 896 x 16384 in 128 x 128 tiles: 2 splits, 83 against 115 us).
-  int splits = 1;
-  const int slots = (per_cu(c) >= 2 ? 2 : 1) * info->cus;
-  if (const char* e = getenv("DG_SPLIT_K")) splits = atoi(e);
-  else if (c->sched != dg::kPingPong && p.num_tiles * 2 <= slots && p.kb_count >= 4) {
-    splits = slots / p.num_tiles;
-    // no more splits than it takes to shorten the longest one
-    while (splits > 1 && (p.kb_count + splits - 2) / (splits - 1) == (p.kb_count + splits - 1) / splits) --splits;
-    const int min_split_slabs = 2;
-    if (splits > p.kb_count / min_split_slabs) splits = p.kb_count / min_split_slabs;
-    if (splits > 8) splits = 8;  // partial-tile traffic grows with the count
-  }
-  if (splits > 1) {
-    const int per = (p.kb_count + splits - 1) / splits;
-    splits = (p.kb_count + per - 1) / per;  // no empty splits
-    p.splits = splits;
-    p.split_slabs = per;
-  }
+  p.splits = dense_splits(c, p.num_tiles, p.kb_count, info, &p.split_slabs);
   if (p.splits > 1) {
     if (c->sched == dg::kPingPong)
       return fail(DG_ERR_INVALID_ARGUMENT, "configuration %s does not support split-K", c->name);
@@ -418,6 +449,9 @@ int dg_get_m_alignment_for_contiguous_layout(void) { return 128; }
 
 int dg_get_sfa_ld(int m) { return m < 0 ? 0 : sfa_ld(m); }
 
+static_assert(DG_DTYPE_FP8 == dg::kFp8 && DG_DTYPE_BF16 == dg::kBf16 && DG_DTYPE_FP4 == dg::kFp4,
+              "dtype codes of the ABI and the kernels agree");
+
 const char* dg_version(void) { return "dg-gfx950 0.1"; }
 
 int dg_reserve_workspace(size_t bytes) {
@@ -427,6 +461,45 @@ int dg_reserve_workspace(size_t bytes) {
   float* part;
   int* cnt;
   if (int s = ensure_workspace(dev, bytes, &part, &cnt)) return s;
+  return ok();
+}
+
+int dg_dense_workspace_size(int dtype, int m, int n, int k, size_t* bytes) {
+  if (!bytes) return fail(DG_ERR_INVALID_ARGUMENT, "null pointer argument");
+  *bytes = 0;
+  int k_bytes = 0;
+  switch (dtype) {
+    case DG_DTYPE_FP8:
+      if (k < 128 || k % 128 != 0)
+        return fail(DG_ERR_UNSUPPORTED_SHAPE, "k must be a positive multiple of 128 (got %d)", k);
+      k_bytes = k;
+      break;
+    case DG_DTYPE_BF16:
+      if (k < 64 || k % 64 != 0 || k > (1 << 30))
+        return fail(DG_ERR_UNSUPPORTED_SHAPE, "k must be a positive multiple of 64 (got %d)", k);
+      k_bytes = 2 * k;
+      break;
+    case DG_DTYPE_FP4:
+      if (k < 256 || k % 256 != 0)
+        return fail(DG_ERR_UNSUPPORTED_SHAPE, "k must be a positive multiple of 256 (got %d)", k);
+      k_bytes = k / 2;
+      break;
+    default:
+      return fail(DG_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+  }
+  if (m < 0) return fail(DG_ERR_INVALID_ARGUMENT, "m must be >= 0 (got %d)", m);
+  if (n < 1) return fail(DG_ERR_INVALID_ARGUMENT, "n must be >= 1 (got %d)", n);
+  if (m == 0) return ok();
+  int dev;
+  DeviceInfo* info;
+  if (int s = current_device(&dev, &info)) return s;
+  if (int s = ensure_kernel_attributes()) return s;
+  const Config* c;
+  if (int s = dense_config(dtype, m, n, info, &c)) return s;
+  const long long tiles = (long long)((m + c->bm - 1) / c->bm) * ((n + c->bn - 1) / c->bn);
+  int per = 0;
+  const int splits = dense_splits(c, (int)tiles, k_bytes / 128, info, &per);
+  if (splits > 1) *bytes = (size_t)tiles * splits * c->bm * c->bn * sizeof(float);
   return ok();
 }
 
@@ -464,13 +537,7 @@ int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const f
   DeviceInfo* info;
   if (int s = current_device(&dev, &info)) return s;
   const Config* c;
-  if (int s = forced_config(dg::kDense, &c)) return s;
-  if (!c) {
-    if (m <= 64) c = find_config(n <= 4096 ? "dense_64x32_w4_s4" : "dense_64x64_w4_s3", dg::kDense);
-    else if (m <= 256 || n <= 256 || !big_tiles_enough(m, n, info))
-      c = find_config("dense_128x128_w4_s2", dg::kDense);
-    else c = find_config("dense_256x256_w8_s2", dg::kDense);
-  }
+  if (int s = dense_config(dg::kFp8, m, n, info, &c)) return s;
   dg::GemmParams p{};
   p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d;
   return launch_dense(c, p, dev, info, m, n, k, k / 128, stream);
@@ -490,13 +557,7 @@ int dg_bf16_gemm_nt(const uint16_t* a, const uint16_t* b, uint16_t* d, int m, in
   DeviceInfo* info;
   if (int s = current_device(&dev, &info)) return s;
   const Config* c;
-  if (int s = forced_config(dg::kDense, &c, dg::kBf16)) return s;
-  if (!c) {
-    if (m <= 64) c = find_config("bf16_64x32_w4_s4", dg::kDense, dg::kBf16);
-    else if (m <= 256 || n <= 256 || !big_tiles_enough(m, n, info))
-      c = find_config("bf16_128x128_w4_s2", dg::kDense, dg::kBf16);
-    else c = find_config("bf16_256x256_w8_s2", dg::kDense, dg::kBf16);
-  }
+  if (int s = dense_config(dg::kBf16, m, n, info, &c)) return s;
   dg::GemmParams p{};
   p.a = reinterpret_cast<const uint8_t*>(a);
   p.b = reinterpret_cast<const uint8_t*>(b);
@@ -520,13 +581,7 @@ int dg_fp4_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const f
   DeviceInfo* info;
   if (int s = current_device(&dev, &info)) return s;
   const Config* c;
-  if (int s = forced_config(dg::kDense, &c, dg::kFp4)) return s;
-  if (!c) {
-    if (m <= 64) c = find_config("fp4_64x32_w4_s4", dg::kDense, dg::kFp4);
-    else if (m <= 256 || n <= 256 || !big_tiles_enough(m, n, info))
-      c = find_config("fp4_128x128_w4_s2", dg::kDense, dg::kFp4);
-    else c = find_config("fp4_256x256_w8_s2", dg::kDense, dg::kFp4);
-  }
+  if (int s = dense_config(dg::kFp4, m, n, info, &c)) return s;
   dg::GemmParams p{};
   p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d;
   return launch_dense(c, p, dev, info, m, n, k / 2, k / 128, stream);

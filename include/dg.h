@@ -72,13 +72,14 @@ typedef enum {
  * Dense FP8 NT GEMM: D[m][n] = A[m][k] . B[n][k]^T with 1x128 (A) and
  * 128x128 (B) fp32 block scales.  Rows m and columns n may be any size >= 0
  * and >= 1 respectively; a partial last 128-row block of B uses its own scale
- * row of sfb.  When the output tiles alone cannot fill the GPU (skinny m),
- * the K dimension is split over several workgroups whose fp32 partial tiles
- * meet in a library-owned device workspace and are added in a fixed order,
- * so results stay bit-for-bit reproducible.  The workspace is allocated (or
- * grown) by the first call that needs it on a device; that call is then not
- * graph-capturable (dg_reserve_workspace avoids this), and concurrent
- * split-K calls on one device must not overlap in time.
+ * row of sfb.  When the output tiles alone cannot fill the GPU (skinny m,
+ * or few tiles, as in one GPU's shard of a larger GEMM), the K dimension is
+ * split over several workgroups whose fp32 partial tiles meet in a
+ * library-owned device workspace and are added in a fixed order, so results
+ * stay bit-for-bit reproducible.  The workspace is allocated (or grown) by
+ * the first call that needs it on a device; that call is then not
+ * graph-capturable (dg_reserve_workspace with dg_dense_workspace_size avoids
+ * this), and concurrent split-K calls on one device must not overlap in time.
  */
 int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
                    uint16_t* d, int m, int n, int k, dg_stream_t stream);
@@ -240,6 +241,20 @@ int dg_quantize_b_128x128_fp4(const float* x, uint8_t* q, float* sfb, int n, int
  * when it has to grow the workspace.
  */
 int dg_reserve_workspace(size_t bytes);
+
+/* Operand types of the dense entry points, for dg_dense_workspace_size. */
+typedef enum { DG_DTYPE_FP8 = 0, DG_DTYPE_BF16 = 1, DG_DTYPE_FP4 = 2 } dg_dtype;
+
+/*
+ * Bytes of split-K workspace that a dense call of this dtype and shape
+ * (dg_fp8_gemm_nt, dg_bf16_gemm_nt or dg_fp4_gemm_nt, m x n, K of k values)
+ * makes on the current device: 0 when the call does not split K.  Passing
+ * it to dg_reserve_workspace before capturing such calls in a graph keeps
+ * them from allocating.  Same shape checks as the GEMM calls (k a positive
+ * multiple of 128, 64 or 256 for fp8, bf16 and fp4, m >= 0, n >= 1), an
+ * unknown dtype is DG_ERR_INVALID_ARGUMENT, and *bytes is 0 on any error.
+ */
+int dg_dense_workspace_size(int dtype, int m, int n, int k, size_t* bytes);
 
 /* Static text for a status code. */
 const char* dg_status_string(int status);

@@ -129,12 +129,28 @@ def test_quant_validation(lib):
     assert lib.dg_quantize_b_128x128(GOOD, GOOD, GOOD, 0, 128, None) == 0
 
 
+def test_workspace_size_validation(lib):
+    out = ctypes.c_size_t(7)
+    size = lambda *a: lib.dg_dense_workspace_size(*a, ctypes.byref(out))
+    assert lib.dg_dense_workspace_size(0, 64, 64, 128, None) == 1       # null result pointer
+    assert size(3, 64, 64, 128) == 1 and out.value == 0                 # unknown dtype
+    assert size(0, 64, 64, 100) == 2                                    # fp8: k % 128
+    assert size(1, 64, 64, 96) == 2                                     # bf16: k % 64
+    assert size(2, 64, 64, 128) == 2                                    # fp4: k % 256
+    assert size(0, -1, 64, 128) == 1 and size(0, 64, 0, 128) == 1
+    out.value = 7
+    assert size(0, 0, 64, 128) == 0 and out.value == 0                  # m = 0: no split, no device needed
+    with pytest.raises(ValueError):
+        dg.dense_workspace_size(64, 64, 128, dtype="fp16")
+
+
 def test_no_device_is_reported_not_crashed(lib):
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     # valid-looking arguments reach the device query, which reports no device
     assert lib.dg_fp8_gemm_nt(GOOD, GOOD, GOOD, GOOD, GOOD, 64, 64, 128, None) == 4
+    assert lib.dg_dense_workspace_size(0, 64, 2112, 7168, ctypes.byref(ctypes.c_size_t())) == 4
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -108,3 +108,36 @@ def test_graph_swiglu_and_fp4(gpu):
     torch.cuda.synchronize()
     refs = eager_refs()
     _replay_check(graph, [hq, hs, d4], refs, run, "swiglu + fp4, new counts")
+
+
+def test_workspace_size_then_graph_of_mid_shape(gpu):
+    """dense_workspace_size gives what a dense call's split-K takes (known
+    figures on the decode, large and N-shard shapes); with that much
+    reserved, a split-K call of a mid-sized shape captures and replays like
+    its eager run."""
+    tile = 64 * 32 * 4
+    for dt in ("fp8", "bf16", "fp4"):
+        assert dg.dense_workspace_size(64, 2112, 7168, dt) == 66 * 7 * tile, dt  # 7 splits of 64 x 32 tiles
+    assert dg.dense_workspace_size(4096, 7168, 16384) == 0                       # 448 big tiles, no split
+    assert dg.dense_workspace_size(4096, 896, 16384) == 224 * 2 * 128 * 128 * 4  # 128 x 128 tiles, 2 splits
+    assert dg.dense_workspace_size(0, 896, 16384) == 0
+    m, n, k = 1024, 896, 2048  # 56 tiles of 128 x 128, 8 splits
+    need = dg.dense_workspace_size(m, n, k)
+    assert need == 56 * 8 * 128 * 128 * 4
+    dg.reserve_workspace(need)
+    rng = np.random.default_rng(5)
+    qa, sfa = dg.quantize_a_1x128(torch.from_numpy(rng.standard_normal((m, k), dtype=np.float32)).to(gpu))
+    qb, sfb = dg.quantize_b_128x128(torch.from_numpy(rng.standard_normal((n, k), dtype=np.float32)).to(gpu))
+    d_eager = torch.empty((m, n), dtype=torch.bfloat16, device=gpu)
+    dg.fp8_gemm_nt((qa, sfa), (qb, sfb), d_eager)
+    torch.cuda.synchronize()
+    ref = d_eager.view(torch.uint8).cpu().numpy()
+    d = torch.empty_like(d_eager)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    print("[case] graph capture of a split-K mid shape 1024x896x2048", flush=True)
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            dg.fp8_gemm_nt((qa, sfa), (qb, sfb), d)
+    torch.cuda.synchronize()
+    _replay_check(graph, [d], [ref], lambda: dg.fp8_gemm_nt((qa, sfa), (qb, sfb), d_eager), "mid shape")
