@@ -107,8 +107,11 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, cons
  * num_groups entries, clamped on the device to [0, max_m]) says how many
  * leading rows are valid.  Only valid rows are computed and written, so the
  * shapes never change and the call suits graph capture.  expected_m is a
- * host-side hint of the typical valid count (0 = unknown); it only steers
- * the tile choice and never changes results.
+ * host-side hint of the typical valid count per expert (0 = unknown); it
+ * only steers the tile choice (a count up to 80 favours the schedule that
+ * streams B fastest, larger or unknown ones the schedule that overlaps the
+ * fullest experts' MFMA work) and never changes results beyond the
+ * tolerance of the GEMM.
  */
 int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const uint8_t* b,
                                     const float* sfb, uint16_t* d, const int32_t* masked_m,

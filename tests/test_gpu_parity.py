@@ -134,6 +134,32 @@ def test_masked(gpu, cfg, max_m, monkeypatch):
     assert H.guard_untouched(flat, d.numel())
 
 
+def test_masked_expected_m_steers_schedule_only(gpu):
+    # expected_m 0 (unknown) and 150 keep the ping-pong schedule, 1..80 the
+    # interleaved one; each is checked against the oracle, and all give the
+    # same bits (both promote every slab in the same order)
+    g, max_m, n, k = 5, 256, 512, 640
+    masked_m = np.array([40, 0, 256, 7, 129], dtype=np.int32)
+    x = W.draw_masked(g, max_m, n, k, seed=21, masked_m=masked_m)
+    qas = [oracle.quantize_a_1x128(x["a"][i]) for i in range(g)]
+    qa = np.stack([q for q, _ in qas])
+    sa = np.stack([s for _, s in qas])
+    qbs = [oracle.quantize_b_128x128(x["b"][i]) for i in range(g)]
+    qb = np.stack([q for q, _ in qbs])
+    sb = np.stack([s for _, s in qbs])
+    r, valid = oracle.grouped_masked_ref(qa, sa, qb, sb, masked_m)
+    bits = []
+    for em in (0, 32, 80, 81, 150):
+        print(f"[case] masked expected_m={em}", flush=True)
+        d, flat = H.run_masked(qa, sa, qb, sb, masked_m, gpu, expected_m=em)
+        res = oracle.tolerance_check(H.d_float(d), r, valid[:, :, None])
+        assert res["ok"], (em, res)
+        assert H.guard_untouched(flat, d.numel())
+        bits.append(H.d_bits(d))
+    for b in bits[1:]:
+        assert np.array_equal(b, bits[0])
+
+
 def test_unknown_forced_config_is_an_error(gpu, monkeypatch):
     monkeypatch.setenv("DG_FORCE_CONFIG", "no_such_config")
     qa, sa, qb, sb = dense_case(64, 64, 128, seed=1)

@@ -144,13 +144,16 @@ def test_contiguous_full(gpu):
         check_sampled(f"{name} expert {e}", d_sel.astype(np.float64), qa_r, sa_r, b_codes, b_scales, rows, cols)
 
 
-def test_masked_full(gpu):
-    name = "moe_masked_16x256_n4096_k7168"
+@pytest.mark.parametrize("name,total", [("moe_masked_16x256_n4096_k7168", 2067),
+                                        ("moe_masked_16x256_c64_n4096_k7168", 518)])
+def test_masked_full(gpu, name, total):
+    # the typical count passed as expected_m picks the ping-pong schedule for
+    # the first workload (mean 129) and the interleaved one for the second (32)
     w = W.WORKLOADS[name]
     g, max_m, n, k = w.shape["g"], w.shape["max_m"], w.shape["n"], w.shape["k"]
     x = W.draw(name)
     mm = x["masked_m"]
-    assert int(mm.sum()) == 2067
+    assert int(mm.sum()) == total
     print(f"[case] {name}: quantise + GEMM on GPU", flush=True)
     qa, sfa = dg.quantize_a_1x128(H.f32_to_device(x["a"], gpu))
     qb, sfb = dg.quantize_b_128x128(H.f32_to_device(x["b"], gpu))

@@ -58,6 +58,12 @@ WORKLOADS = {
         "moe_masked_16x256_n4096_k7168", "masked",
         "MoE grouped masked decode, 16 experts, max_m=256, N=4096 K=7168",
         g=16, max_m=256, n=4096, k=7168, b_std=0.02),
+    # The masked decode shape with lighter experts: counts uniform on 0..64
+    # (about 32 tokens per expert, the low-batch decode regime), same buffers
+    "moe_masked_16x256_c64_n4096_k7168": Workload(
+        "moe_masked_16x256_c64_n4096_k7168", "masked",
+        "MoE grouped masked decode, 16 experts, max_m=256, counts U{0..64}, N=4096 K=7168",
+        g=16, max_m=256, n=4096, k=7168, b_std=0.02, count_hi=64),
     # FP4 (e2m1) dense GEMM on the large dense shape, drawn as that shape
     "fp4_dense_4096x7168x16384": Workload(
         "fp4_dense_4096x7168x16384", "fp4", "FP4 dense GEMM (M=4096 N=7168 K=16384)",
@@ -122,13 +128,14 @@ def draw_contiguous(group_rows, n, k, seed=0, b_std=0.02):
     return {"a": a, "b": b, "m_indices": m_indices}
 
 
-def draw_masked(g, max_m, n, k, seed=0, b_std=0.02, masked_m=None):
-    """First masked_m ~ Uniform{0..max_m} per expert (unless given), then A
-    (g x max_m x k) ~ N(0,1) with the invalid rows drawn too, then B
-    (g x n x k) ~ N(0, b_std^2)."""
+def draw_masked(g, max_m, n, k, seed=0, b_std=0.02, masked_m=None, count_hi=None):
+    """First masked_m ~ Uniform{0..count_hi} per expert (count_hi defaults to
+    max_m; unless masked_m is given), then A (g x max_m x k) ~ N(0,1) with
+    the invalid rows drawn too, then B (g x n x k) ~ N(0, b_std^2)."""
     rng = np.random.default_rng(seed)
     if masked_m is None:
-        masked_m = rng.integers(0, max_m + 1, g).astype(np.int32)
+        hi = max_m if count_hi is None else count_hi
+        masked_m = rng.integers(0, hi + 1, g).astype(np.int32)
     else:
         masked_m = np.asarray(masked_m, dtype=np.int32)
     a = _normal(rng, (g, max_m, k), 1.0)
@@ -159,7 +166,7 @@ def draw(name, seed=0):
         return draw_kgrouped(s["k_sizes"], s["m"], s["n"], seed, s["b_std"])
     if w.kind == "swiglu":
         return draw_masked(s["g"], s["max_m"], 2 * s["inter"], s["k"], seed, s["b_std"])
-    return draw_masked(s["g"], s["max_m"], s["n"], s["k"], seed, s["b_std"])
+    return draw_masked(s["g"], s["max_m"], s["n"], s["k"], seed, s["b_std"], count_hi=s.get("count_hi"))
 
 
 def algorithmic_work(kind, **p):
