@@ -137,6 +137,7 @@ const Config* configs(int* count) {
       make_config<256, 128, 1, 4, 2, dg::kMasked>("masked_256x128_w4_s2"),
       make_config<256, 128, 1, 4, 3, dg::kMasked>("masked_256x128_w4_s3"),
       make_config<64, 64, 1, 4, 3, dg::kMasked>("masked_64x64_w4_s3"),
+      make_config<128, 256, 2, 4, 3, dg::kMasked>("masked_128x256_w8_s3"),
       // K-grouped
       make_config<256, 256, 2, 4, 2, dg::kKGrouped>("kgrouped_256x256_w8_s2"),
       make_config<128, 128, 2, 2, 2, dg::kKGrouped>("kgrouped_128x128_w4_s2"),
@@ -621,16 +622,28 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, cons
   return launch(*c, p, p.num_tiles, (hipStream_t)stream);
 }
 
-// Masked layout: the 256 x 256 tile's interleaved schedule streams an
-// expert's B faster than the ping-pong schedule, which wins once the MFMA
-// work of the fullest experts dominates.  With 16 experts, max_m 256,
-// N 4096, K 7168 and counts uniform on 0..c (one process, same inputs):
-// c = 16..128 (mean 8..64) 88-110 against 117-124 us; c = 160 123 against
-// 128 us; c = 192 140 against 131 us; c = 256 160-164 against 139 us.  The
-// SwiGLU epilogue moves the same way (101-129 against 127-136 us up to
-// c = 160).  A typical count (expected_m) up to 80 picks the interleaved
-// schedule; 0 (unknown) keeps the ping-pong one.
-bool light_experts(int expected_m) { return expected_m > 0 && expected_m <= 80; }
+// Masked-layout tiles (16 experts, max_m 256, N 4096, K 7168, counts uniform
+// on 0..c, one process, same inputs; the 256-column tiles of the SwiGLU
+// epilogue move the same way):
+//  * while every expert fits one 128-row tile, 128 x 256 tiles with three
+//    LDS stages stream B fastest: 77-85 us for c = 16-64 (6.1-5.6 TB/s) and
+//    108 us for c = 128, against 90-113 us for the 256 x 256 interleaved
+//    schedule and 118-124 us for the ping-pong one.  An expert past 128 rows
+//    needs a second row of tiles that waits for a free CU (one workgroup per
+//    CU): 166-202 us for c = 160-256.
+//  * the 256 x 256 interleaved schedule leads up to c = 160 (123 against
+//    128 us), the ping-pong one from c = 192 (131-139 against 140-164 us).
+// So: max_m <= 128 (no expert can pass 128 rows) or a typical count
+// (expected_m) up to 48 picks the 128-row tile when there are enough of its
+// tiles to cover half the CUs; a typical count up to 80 the interleaved
+// 256 x 256 schedule; larger or unknown (0) counts the ping-pong one.
+enum class MaskedTile { kRows128, kInterleaved, kPingPong };
+MaskedTile masked_tile(int num_groups, int max_m, int n, int expected_m, const DeviceInfo* info) {
+  const bool enough = 2LL * num_groups * ((n + 255) / 256) >= info->cus;
+  if (enough && (max_m <= 128 || (expected_m > 0 && expected_m <= 48))) return MaskedTile::kRows128;
+  if (expected_m > 0 && expected_m <= 80) return MaskedTile::kInterleaved;
+  return MaskedTile::kPingPong;
+}
 
 int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const uint8_t* b,
                                     const float* sfb, uint16_t* d, const int32_t* masked_m,
@@ -652,11 +665,14 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const ui
   if (int s = current_device(&dev, &info)) return s;
   const Config* c;
   if (int s = forced_config(dg::kMasked, &c)) return s;
-  if (!c)
-    c = find_config(max_m <= 64 ? "masked_64x64_w4_s3"
-                    : light_experts(expected_m) ? "masked_256x256_w8_s2"
-                                                : "masked_256x256_w8_s2_pp",
+  if (!c) {
+    const MaskedTile t = masked_tile(num_groups, max_m, n, expected_m, info);
+    c = find_config(t == MaskedTile::kRows128 ? "masked_128x256_w8_s3"
+                    : max_m <= 64             ? "masked_64x64_w4_s3"
+                    : t == MaskedTile::kInterleaved ? "masked_256x256_w8_s2"
+                                                    : "masked_256x256_w8_s2_pp",
                     dg::kMasked);
+  }
   dg::GemmParams p{};
   p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.masked_m = masked_m;
   p.num_groups = num_groups;
@@ -715,11 +731,14 @@ int dg_m_grouped_fp8_gemm_nt_masked_swiglu(const uint8_t* a, const float* sfa, c
   if (int s = current_device(&dev, &info)) return s;
   const Config* c;
   if (int s = forced_config(dg::kMasked, &c, dg::kFp8, dg::kEpiSwigluFp8)) return s;
-  if (!c)
-    c = find_config(max_m <= 64 ? "swiglu_64x256_w4_s3"
-                    : light_experts(expected_m) ? "swiglu_256x256_w8_s2"
-                                                : "swiglu_256x256_w8_s2_pp",
+  if (!c) {
+    const MaskedTile t = masked_tile(num_groups, max_m, 2 * inter, expected_m, info);
+    c = find_config(t == MaskedTile::kRows128 ? "swiglu_128x256_w8_s3"
+                    : max_m <= 64             ? "swiglu_64x256_w4_s3"
+                    : t == MaskedTile::kInterleaved ? "swiglu_256x256_w8_s2"
+                                                    : "swiglu_256x256_w8_s2_pp",
                     dg::kMasked, dg::kFp8, dg::kEpiSwigluFp8);
+  }
   dg::GemmParams p{};
   p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.masked_m = masked_m;
   p.hq = hq; p.hs = hs; p.inter = inter;

@@ -108,10 +108,12 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, cons
  * leading rows are valid.  Only valid rows are computed and written, so the
  * shapes never change and the call suits graph capture.  expected_m is a
  * host-side hint of the typical valid count per expert (0 = unknown); it
- * only steers the tile choice (a count up to 80 favours the schedule that
- * streams B fastest, larger or unknown ones the schedule that overlaps the
- * fullest experts' MFMA work) and never changes results beyond the
- * tolerance of the GEMM.
+ * only steers the tile choice and never changes results (every tile gives
+ * the same bits).  Counts up to 48 pick 128-row tiles, which stream B
+ * fastest while every expert fits 128 rows but slow down when one does not
+ * (max_m <= 128 picks them in any case); counts up to 80 a 256-row tile
+ * with the same streaming schedule; larger or unknown counts the schedule
+ * that overlaps the fullest experts' MFMA work with their loads.
  */
 int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const uint8_t* b,
                                     const float* sfb, uint16_t* d, const int32_t* masked_m,

@@ -111,7 +111,8 @@ def test_contiguous(gpu, cfg, monkeypatch):
                                        ("masked_256x128_w4_s3", 200), ("masked_64x64_w4_s3", 130),
                                        ("masked_256x256_w8_s2", 300), ("masked_256x256_w8_s2_pp", 300),
                                        ("masked_256x256_w8_s2_pp", 200), ("masked_256x128_w8_s2", 300),
-                                       ("masked_256x128_w8_s2", 100)])
+                                       ("masked_256x128_w8_s2", 100), ("masked_128x256_w8_s3", 300),
+                                       ("masked_128x256_w8_s3", 100)])
 def test_masked(gpu, cfg, max_m, monkeypatch):
     if cfg:
         monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
@@ -154,6 +155,38 @@ def test_masked_expected_m_steers_schedule_only(gpu):
         d, flat = H.run_masked(qa, sa, qb, sb, masked_m, gpu, expected_m=em)
         res = oracle.tolerance_check(H.d_float(d), r, valid[:, :, None])
         assert res["ok"], (em, res)
+        assert H.guard_untouched(flat, d.numel())
+        bits.append(H.d_bits(d))
+    for b in bits[1:]:
+        assert np.array_equal(b, bits[0])
+
+
+@pytest.mark.parametrize("max_m,counts", [
+    (256, [40, 0, 256, 7, 129, 128, 1, 90]),   # experts past 128 rows: second row of 128-row tiles
+    (128, [128, 0, 64, 1, 127, 33, 100, 12]),  # max_m 128: the 128-row tile whatever the hint
+])
+def test_masked_tile_rule_wide(gpu, max_m, counts):
+    # 8 experts x 16 column tiles cover half the CUs, so hints up to 48 (and
+    # max_m <= 128) take the 128-row tile, up to 80 the 256-row interleaved
+    # schedule, else ping-pong: every choice matches the oracle with the
+    # same bits
+    g, n, k = 8, 4096, 256
+    masked_m = np.array(counts, dtype=np.int32)
+    x = W.draw_masked(g, max_m, n, k, seed=23, masked_m=masked_m)
+    qas = [oracle.quantize_a_1x128(x["a"][i]) for i in range(g)]
+    qa = np.stack([q for q, _ in qas])
+    sa = np.stack([s for _, s in qas])
+    qbs = [oracle.quantize_b_128x128(x["b"][i]) for i in range(g)]
+    qb = np.stack([q for q, _ in qbs])
+    sb = np.stack([s for _, s in qbs])
+    r, valid = oracle.grouped_masked_ref(qa, sa, qb, sb, masked_m)
+    bits = []
+    for em in (0, 16, 48, 64, 100):
+        print(f"[case] masked wide max_m={max_m} expected_m={em}", flush=True)
+        d, flat = H.run_masked(qa, sa, qb, sb, masked_m, gpu, expected_m=em)
+        res = oracle.tolerance_check(H.d_float(d), r, valid[:, :, None])
+        assert res["ok"], (em, res)
+        assert np.all(H.d_bits(d)[~valid] == H.SENTINEL)
         assert H.guard_untouched(flat, d.numel())
         bits.append(H.d_bits(d))
     for b in bits[1:]:

@@ -219,6 +219,24 @@ def test_deterministic_and_expected_m_hint(gpu):
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+def test_tile_rule_wide_same_bits(gpu):
+    # 8 experts x 16 h blocks: hints 16 / 64 / 0 take the 128-row tile, the
+    # 256-row interleaved schedule and ping-pong; one of them is checked
+    # against the oracle and all give the same codes and scales
+    g, max_m, inter, k = 8, 256, 2048, 256
+    qa, sa, qb, sb, mm = workload_case(g, max_m, inter, k, [40, 0, 256, 7, 129, 128, 1, 90], seed=9)
+    outs = []
+    for em in (16, 64, 0):
+        print(f"[case] swiglu wide expected_m={em}", flush=True)
+        hq, hs, fq, fs = H.run_swiglu(qa, sa, qb, sb, mm, gpu, expected_m=em)
+        assert H.swiglu_guards_untouched(fq, fs, hq.size, hs.size)
+        outs.append((hq, hs))
+    code_share, _ = check_call(outs[0][0], outs[0][1], qa, sa, qb, sb, mm, rule_tol, "wide", 0.15)
+    assert code_share >= 0.98, code_share
+    for hq, hs in outs[1:]:
+        assert np.array_equal(hq, outs[0][0]) and np.array_equal(hs, outs[0][1])
+
+
 def test_feeds_the_second_gemm(gpu):
     """hq/hs are the masked GEMM's A operand as they stand: FC2 over the
     kernel's h matches FC2 over the oracle's h within the GEMM rule plus what
