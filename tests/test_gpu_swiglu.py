@@ -290,17 +290,19 @@ def test_feeds_the_second_gemm(gpu):
         print(f"  expert {e}: {res['n_bad']} of {res['n']} outside the plain GEMM rule", flush=True)
 
 
-def test_full_size_sampled(gpu):
-    """The SwiGLU workload (16 experts, max_m 256, 2I = 4096, I = 2048,
-    K = 7168), run as the benchmark runs it: quantised on the GPU by
-    the library, the fused kernel at its default configuration.  For four
-    experts the oracle re-quantises the expert's A rows and B on the CPU
-    (the codes and scales must be bit-identical) and computes h for the
-    first, last and a middle valid row."""
+@pytest.mark.parametrize("name", ["moe_swiglu_16x256_i2048_k7168", "moe_swiglu_16x256_c64_i2048_k7168"])
+def test_full_size_sampled(gpu, name):
+    """The SwiGLU workloads (16 experts, max_m 256, 2I = 4096, I = 2048,
+    K = 7168; counts up to 256, or up to 64), run as the benchmark runs them:
+    quantised on the GPU by the library, the fused kernel at its default
+    configuration for the mean count as expected_m (ping-pong 256 x 256, or
+    the 128 x 256 tile).  For four experts the oracle re-quantises the
+    expert's A rows and B on the CPU (the codes and scales must be
+    bit-identical) and computes h for the first, last and a middle valid
+    row."""
     import torch
 
     import fp8_block_scaled_nt_amd as dg
-    name = "moe_swiglu_16x256_i2048_k7168"
     x = W.draw(name)
     s = W.WORKLOADS[name].shape
     g, max_m, inter, k = s["g"], s["max_m"], s["inter"], s["k"]

@@ -75,6 +75,11 @@ WORKLOADS = {
         "moe_swiglu_16x256_i2048_k7168", "swiglu",
         "MoE FC1 + SwiGLU + requantise, masked layout, 16 experts, max_m=256, I=2048 K=7168",
         g=16, max_m=256, inter=2048, k=7168, b_std=0.02),
+    # the same with the light-expert counts (uniform on 0..64)
+    "moe_swiglu_16x256_c64_i2048_k7168": Workload(
+        "moe_swiglu_16x256_c64_i2048_k7168", "swiglu",
+        "MoE FC1 + SwiGLU + requantise, masked layout, 16 experts, max_m=256, counts U{0..64}, I=2048 K=7168",
+        g=16, max_m=256, inter=2048, k=7168, b_std=0.02, count_hi=64),
     # BF16 dense GEMM on the large dense shape (operands rounded to bf16 by
     # the caller from these fp32 draws)
     "bf16_dense_4096x7168x16384": Workload(
@@ -165,7 +170,7 @@ def draw(name, seed=0):
     if w.kind == "kgrouped":
         return draw_kgrouped(s["k_sizes"], s["m"], s["n"], seed, s["b_std"])
     if w.kind == "swiglu":
-        return draw_masked(s["g"], s["max_m"], 2 * s["inter"], s["k"], seed, s["b_std"])
+        return draw_masked(s["g"], s["max_m"], 2 * s["inter"], s["k"], seed, s["b_std"], count_hi=s.get("count_hi"))
     return draw_masked(s["g"], s["max_m"], s["n"], s["k"], seed, s["b_std"], count_hi=s.get("count_hi"))
 
 
