@@ -295,6 +295,15 @@ void fill_common(dg::GemmParams& p, const Config& c, int m, int n, int k) {
   if (const char* e = getenv("DG_GROUP_M")) p.group_m = atoi(e) > 0 ? atoi(e) : 4;
 }
 
+// The launch grid is 32-bit: the output tiles (times a split count of up to
+// 8) must fit it.
+int set_num_tiles(dg::GemmParams& p, long long groups) {
+  const long long t = groups * p.tiles_m * (long long)p.tiles_n;
+  if (t > (1LL << 27)) return fail(DG_ERR_UNSUPPORTED_SHAPE, "too many output tiles (%lld)", t);
+  p.num_tiles = (int)t;
+  return DG_OK;
+}
+
 int check_k_n(int n, int k) {
   if (n < 1) return fail(DG_ERR_INVALID_ARGUMENT, "n must be >= 1 (got %d)", n);
   if (k < 128 || k % 128 != 0)
@@ -388,13 +397,15 @@ int launch_dense(const Config* c, dg::GemmParams& p, int dev, const DeviceInfo* 
   p.num_groups = 1;
   fill_common(p, *c, m, n, k_bytes);
   p.sk_count = scale_slabs;
-  p.num_tiles = p.tiles_m * p.tiles_n;
+  if (int s = set_num_tiles(p, 1)) return s;
   p.splits = dense_splits(c, p.num_tiles, p.kb_count, info, &p.split_slabs);
   if (p.splits > 1) {
     if (c->sched == dg::kPingPong)
       return fail(DG_ERR_INVALID_ARGUMENT, "configuration %s does not support split-K", c->name);
     if ((size_t)p.num_tiles > kCounterInts)
       return fail(DG_ERR_UNSUPPORTED_SHAPE, "too many tiles for split-K (%d)", p.num_tiles);
+    if ((long long)p.num_tiles * p.splits > 0x7FFFFFFFLL)
+      return fail(DG_ERR_UNSUPPORTED_SHAPE, "split-K grid too large (%d x %d)", p.num_tiles, p.splits);
     const size_t part = (size_t)p.num_tiles * p.splits * c->bm * c->bn * sizeof(float);
     if (int s = ensure_workspace(dev, part, &p.ws_partial, &p.ws_count)) return s;
   }
@@ -498,6 +509,7 @@ int dg_dense_workspace_size(int dtype, int m, int n, int k, size_t* bytes) {
   const Config* c;
   if (int s = dense_config(dtype, m, n, info, &c)) return s;
   const long long tiles = (long long)((m + c->bm - 1) / c->bm) * ((n + c->bn - 1) / c->bn);
+  if (tiles > (1LL << 27)) return fail(DG_ERR_UNSUPPORTED_SHAPE, "too many output tiles (%lld)", tiles);
   int per = 0;
   const int splits = dense_splits(c, (int)tiles, k_bytes / 128, info, &per);
   if (splits > 1) *bytes = (size_t)tiles * splits * c->bm * c->bn * sizeof(float);
@@ -618,7 +630,7 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, cons
   p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.m_indices = m_indices;
   p.num_groups = num_groups;
   fill_common(p, *c, m, n, k);
-  p.num_tiles = p.tiles_m * p.tiles_n;
+  if (int s = set_num_tiles(p, 1)) return s;
   return launch(*c, p, p.num_tiles, (hipStream_t)stream);
 }
 
@@ -677,7 +689,7 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const ui
   p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.masked_m = masked_m;
   p.num_groups = num_groups;
   fill_common(p, *c, max_m, n, k);
-  p.num_tiles = num_groups * p.tiles_m * p.tiles_n;
+  if (int s = set_num_tiles(p, num_groups)) return s;
   return launch(*c, p, p.num_tiles, (hipStream_t)stream);
 }
 
@@ -704,7 +716,7 @@ int dg_k_grouped_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* 
   p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.k_sizes = k_sizes;
   p.num_groups = num_groups;
   fill_common(p, *c, m, n, k);
-  p.num_tiles = num_groups * p.tiles_m * p.tiles_n;
+  if (int s = set_num_tiles(p, num_groups)) return s;
   p.splits = 1;
   p.split_slabs = p.kb_count;
   return launch(*c, p, p.num_tiles, (hipStream_t)stream);
@@ -745,7 +757,7 @@ int dg_m_grouped_fp8_gemm_nt_masked_swiglu(const uint8_t* a, const float* sfa, c
   p.num_groups = num_groups;
   fill_common(p, *c, max_m, 2 * inter, k);
   p.tiles_n = inter / 128;  // one tile per 128 h columns (128 gate + 128 up rows of B)
-  p.num_tiles = num_groups * p.tiles_m * p.tiles_n;
+  if (int s = set_num_tiles(p, num_groups)) return s;
   return launch(*c, p, p.num_tiles, (hipStream_t)stream);
 }
 

@@ -14,6 +14,7 @@ import os
 import numpy as np
 import pytest
 
+import fp8_block_scaled_nt_amd as dg
 import oracle
 import workloads as W
 from tests import gpu_harness as H
@@ -191,6 +192,19 @@ def test_masked_tile_rule_wide(gpu, max_m, counts):
         bits.append(H.d_bits(d))
     for b in bits[1:]:
         assert np.array_equal(b, bits[0])
+
+
+def test_too_many_tiles_is_rejected(gpu):
+    # each operand stays below 4 GiB, but 2^24 x 2^24 outputs are 2^32 tiles:
+    # the host rejects the call before touching the (fake) pointers
+    import ctypes
+    lib = dg.lib()
+    fake = ctypes.c_void_p(0x10000)
+    big = 1 << 24
+    assert lib.dg_fp8_gemm_nt(fake, fake, fake, fake, fake, big, big, 128, None) == 2
+    assert b"too many output tiles" in lib.dg_last_error_message()
+    out = ctypes.c_size_t(0)
+    assert lib.dg_dense_workspace_size(0, big, big, 128, ctypes.byref(out)) == 2
 
 
 def test_unknown_forced_config_is_an_error(gpu, monkeypatch):
