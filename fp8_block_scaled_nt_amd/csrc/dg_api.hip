@@ -461,7 +461,8 @@ int dg_get_m_alignment_for_contiguous_layout(void) { return 128; }
 
 int dg_get_sfa_ld(int m) { return m < 0 ? 0 : sfa_ld(m); }
 
-static_assert(DG_DTYPE_FP8 == dg::kFp8 && DG_DTYPE_BF16 == dg::kBf16 && DG_DTYPE_FP4 == dg::kFp4,
+static_assert((int)DG_DTYPE_FP8 == (int)dg::kFp8 && (int)DG_DTYPE_BF16 == (int)dg::kBf16 &&
+                  (int)DG_DTYPE_FP4 == (int)dg::kFp4,
               "dtype codes of the ABI and the kernels agree");
 
 const char* dg_version(void) { return "dg-gfx950 0.1"; }

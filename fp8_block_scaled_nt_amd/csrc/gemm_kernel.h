@@ -123,6 +123,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // extra loads are outstanding.  M0 is set inside the asm, with the one wait
 // state the hardware needs before the DMA reads it; nothing else in these
 // kernels keeps a value in M0.
+//
+// M0 must not change until the previous DMA has consumed it.  Measured on
+// gfx950: a wave-wide 16-byte DMA sends its lanes to the texture unit in
+// several passes, and when that unit is busy (several workgroups per CU
+// loading) its last passes (lanes 24-31 and 56-63) can leave after the wave
+// has already executed the next DMA's M0 write; those lanes' bytes then land
+// at the next destination, and the rows they should have filled keep stale
+// data.  Wait states do not bound it (32 still failed under load).  A wave's
+// vector-memory instructions issue in order, so a vector-memory instruction
+// placed ahead of the M0 write holds the write back until the previous DMA
+// has issued in full: each DMA below starts with a load under EXEC = 0, which
+// touches neither memory nor registers.  That load counts in vmcnt like any
+// other (also measured), so every DMA is kVmPerDma vmcnt events.
 typedef int v4i_rsrc __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -140,15 +153,26 @@ __device__ __forceinline__ v4i_rsrc make_rsrc(const void* base, uint32_t bytes) 
   return r;
 }
 
+constexpr int kVmPerDma = 2;  // vmcnt events per lds_dma16 / lds_dma4: the EXEC = 0 load and the DMA
+
+// The EXEC = 0 load names the offset register as its destination: with no
+// lane active nothing is written.
+#define DG_M0_GUARD                                                              \
+  "s_mov_b64 %0, exec\n\ts_mov_b64 exec, 0\n\tbuffer_load_dword %1, %1, %2, 0 offen\n\t" \
+  "s_mov_b64 exec, %0\n\t"
+
 __device__ __forceinline__ void lds_dma16(v4i_rsrc rs, uint32_t voff, uint32_t soff, void* lds_dst) {
-  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(rs), "s"(soff), "s"(lds_addr(lds_dst)) : "memory", "m0");
+  uint64_t exec_save;
+  asm volatile(DG_M0_GUARD "s_mov_b32 m0, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               : "=&s"(exec_save) : "v"(voff), "s"(rs), "s"(soff), "s"(lds_addr(lds_dst)) : "memory", "m0");
 }
 
 __device__ __forceinline__ void lds_dma4(v4i_rsrc rs, uint32_t voff, uint32_t soff, void* lds_dst) {
-  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(rs), "s"(soff), "s"(lds_addr(lds_dst)) : "memory", "m0");
+  uint64_t exec_save;
+  asm volatile(DG_M0_GUARD "s_mov_b32 m0, %4\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               : "=&s"(exec_save) : "v"(voff), "s"(rs), "s"(soff), "s"(lds_addr(lds_dst)) : "memory", "m0");
 }
+#undef DG_M0_GUARD
 
 // Wait until at most N of this wave's vector-memory loads (LDS DMA included)
 // are outstanding; they retire in issue order.  gfx9 s_waitcnt encoding:
@@ -161,7 +185,7 @@ __device__ __forceinline__ void wait_vmem() {
 __device__ __forceinline__ void wait_vmem_all() { wait_vmem<0>(); }
 
 // vmcnt wait with a wave-uniform run-time count (a scalar branch picks the
-// immediate).  Counts above 47 wait for everything.
+// immediate).  Counts above 63, the counter's range, wait for everything.
 __device__ __forceinline__ void wait_vmem_dyn(int n) {
 #define DG_VM_CASE(i) \
   case i:             \
@@ -174,7 +198,9 @@ __device__ __forceinline__ void wait_vmem_dyn(int n) {
     DG_VM_CASE(22) DG_VM_CASE(23) DG_VM_CASE(24) DG_VM_CASE(25) DG_VM_CASE(26) DG_VM_CASE(27) DG_VM_CASE(28)
     DG_VM_CASE(29) DG_VM_CASE(30) DG_VM_CASE(31) DG_VM_CASE(32) DG_VM_CASE(33) DG_VM_CASE(34) DG_VM_CASE(35)
     DG_VM_CASE(36) DG_VM_CASE(37) DG_VM_CASE(38) DG_VM_CASE(39) DG_VM_CASE(40) DG_VM_CASE(41) DG_VM_CASE(42)
-    DG_VM_CASE(43) DG_VM_CASE(44) DG_VM_CASE(45) DG_VM_CASE(46) DG_VM_CASE(47)
+    DG_VM_CASE(43) DG_VM_CASE(44) DG_VM_CASE(45) DG_VM_CASE(46) DG_VM_CASE(47) DG_VM_CASE(48) DG_VM_CASE(49)
+    DG_VM_CASE(50) DG_VM_CASE(51) DG_VM_CASE(52) DG_VM_CASE(53) DG_VM_CASE(54) DG_VM_CASE(55) DG_VM_CASE(56)
+    DG_VM_CASE(57) DG_VM_CASE(58) DG_VM_CASE(59) DG_VM_CASE(60) DG_VM_CASE(61) DG_VM_CASE(62) DG_VM_CASE(63)
     default:
       wait_vmem<0>();
       return;
@@ -670,7 +696,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
     for (int kb = 0; kb < KB; ++kb) {
       // slab kb's DMA must have landed (in every wave: then the barrier); the
       // loads issued after it may stay in flight.
-      wait_vmem_dyn(c_loads * loads_ahead<NST>(kb, KB));
+      wait_vmem_dyn(kVmPerDma * c_loads * loads_ahead<NST>(kb, KB));
       block_barrier();  // also: every wave is done with the stage about to be refilled
       __builtin_amdgcn_sched_barrier(0);
       if (!kSB && kb + NST - 1 < KB) issue_slab(kb + NST - 1, (kb + NST - 1) % NST);

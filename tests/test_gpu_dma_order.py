@@ -1,0 +1,85 @@
+"""Repeated GEMMs where many workgroups per CU load LDS by DMA at once.
+
+Small tiles without split-K on a shape with many tiles (512 x 7168 x 2048
+with 64 x 32 tiles: 1792 workgroups, several on every CU) keep every CU's
+texture unit busy with LDS DMA from several workgroups.  The first call must
+match the oracle element by element, and every later call must repeat its
+bits exactly (without split-K the kernels are deterministic).
+
+This is the regime in which a DMA whose LDS destination register (M0) is
+rewritten for the next DMA before it has issued in full sends its last lanes'
+bytes to the next destination: a few A or B rows of a stage then keep stale
+data, and calls differ from one another (most calls did, before each DMA was
+made to wait for the previous one's issue).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_block_scaled_nt_amd as dg
+import oracle
+import workloads as W
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+M, N, K = 512, 7168, 2048
+CALLS = 32
+
+
+def _fp8(dev):
+    x = W.draw_dense(M, N, K, seed=71)
+    qa, sa = oracle.quantize_a_1x128(x["a"])
+    qb, sb = oracle.quantize_b_128x128(x["b"])
+    a, b = H.codes_to_device(qa, dev), H.codes_to_device(qb, dev)
+    sfa, sfb = H.f32_to_device(H.slab_major(sa), dev), H.f32_to_device(sb, dev)
+    return (lambda d: dg.fp8_gemm_nt((a, sfa), (b, sfb), d)), (lambda: oracle.gemm_nt_ref(qa, sa, qb, sb))
+
+
+def _bf16(dev):
+    x = W.draw_dense(M, N, K, seed=72)
+    a_bits = (np.asarray(x["a"], np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    b_bits = (np.asarray(x["b"], np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    a = torch.from_numpy(a_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    b = torch.from_numpy(b_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    return (lambda d: dg.bf16_gemm_nt(a, b, d)), (lambda: oracle.bf16_gemm_nt_ref(a_bits, b_bits))
+
+
+def _fp4(dev):
+    x = W.draw_dense(M, N, K, seed=73)
+    pa, sa = oracle.quantize_a_1x128_fp4(x["a"])
+    pb, sb = oracle.quantize_b_128x128_fp4(x["b"])
+    a = torch.from_numpy(np.ascontiguousarray(pa, np.uint8)).to(dev)
+    b = torch.from_numpy(np.ascontiguousarray(pb, np.uint8)).to(dev)
+    sfa, sfb = H.f32_to_device(H.slab_major(sa), dev), H.f32_to_device(sb, dev)
+    return (lambda d: dg.fp4_gemm_nt((a, sfa), (b, sfb), d)), (lambda: oracle.fp4_gemm_nt_ref(pa, sa, pb, sb))
+
+
+@pytest.mark.parametrize("make,cfg", [
+    (_fp8, "dense_64x32_w4_s4"),
+    (_fp8, "dense_64x64_w4_s3"),
+    (_bf16, "bf16_64x32_w4_s4"),
+    (_fp4, "fp4_64x32_w4_s4"),
+], ids=["fp8-64x32", "fp8-64x64", "bf16-64x32", "fp4-64x32"])
+def test_repeated_calls_same_bits(gpu, make, cfg, monkeypatch):
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    monkeypatch.setenv("DG_SPLIT_K", "1")
+    print(f"[case] {cfg} {M}x{N}x{K}, {CALLS} calls", flush=True)
+    launch, ref = make(gpu)
+    outs = [H.sentinel_bf16((M, N), gpu)[0] for _ in range(4)]
+    launch(outs[0])
+    torch.cuda.synchronize()
+    res = oracle.tolerance_check(H.d_float(outs[0]), ref())
+    assert res["ok"], (cfg, res)
+    first = outs[0].view(torch.int16).clone()
+    differing = []
+    for c in range(1, CALLS):
+        d = outs[c % 4]
+        d.view(torch.int16).fill_(-1)
+        launch(d)
+        if not torch.equal(d.view(torch.int16), first):
+            bad = int((d.view(torch.int16) != first).sum())
+            differing.append((c, bad))
+    torch.cuda.synchronize()
+    assert not differing, f"{cfg}: calls whose bits differ from the first (call, elements): {differing}"
