@@ -373,9 +373,17 @@ const Config* dense_default_config(int dtype, int m, int n, const DeviceInfo* in
     case dg::kFp4:
       if (m <= 64) return find_config("fp4_64x32_w4_s4", dg::kDense, dg::kFp4);
       return find_config(mid ? "fp4_128x128_w4_s2" : "fp4_256x256_w8_s2", dg::kDense, dg::kFp4);
-    default:
+    default: {
       if (m <= 64) return find_config(n <= 4096 ? "dense_64x32_w4_s4" : "dense_64x64_w4_s3", dg::kDense);
-      return find_config(mid ? "dense_128x128_w4_s2" : "dense_256x256_w8_s2", dg::kDense);
+      if (!mid) return find_config("dense_256x256_w8_s2", dg::kDense);
+      // Few 128 x 128 tiles: smaller tiles (four or more workgroups per CU),
+      // or a third stage, keep more loads in flight per CU than split-K of
+      // the 128 x 128 tile alone does.
+      const long long t128 = (long long)((m + 127) / 128) * ((n + 127) / 128);
+      if (m <= 256 && t128 <= 64) return find_config(n <= 1024 ? "dense_64x32_w4_s4" : "dense_64x64_w4_s3", dg::kDense);
+      if (t128 <= 72 && n >= 1024) return find_config("dense_128x128_w4_s3", dg::kDense);
+      return find_config("dense_128x128_w4_s2", dg::kDense);
+    }
   }
 }
 

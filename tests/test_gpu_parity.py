@@ -251,10 +251,16 @@ def test_dense_split_k(gpu, m, n, k, splits, cfg, monkeypatch):
     (1024, 896, 2048),   # 16 big tiles: 128 x 128 tiles, 8 splits of 2 slabs
     (512, 1792, 1536),   # 56 tiles of 128 x 128 over 6 splits
     (2304, 2304, 512),   # 81 big tiles: 128 x 128, no split (324 tiles, 2 slabs each)
+    (128, 2112, 1024),   # 17 tiles of 128 x 128: 64 x 64 tiles, 3 stages, split-K
+    (256, 512, 1280),    # n <= 1024: 64 x 32 tiles, split-K
+    (384, 2112, 768),    # 51 tiles of 128 x 128: 3 stages
+    (200, 4096, 384),    # a partial 64-row tile row, 3 slabs
 ])
 def test_dense_default_mid_shapes(gpu, m, n, k):
-    # shapes whose 256 x 256 tiles would leave most CUs idle take the
-    # 128 x 128 tiles and, where still too few, split-K
+    # shapes whose 256 x 256 tiles would leave most CUs idle take 128 x 128
+    # tiles (with three stages when they are few), 64 x 64 or 64 x 32 tiles
+    # when m <= 256 and the 128 x 128 tiles are fewer than 65, and split-K
+    # while still too few
     qa, sa, qb, sb = dense_case(m, n, k, seed=m + n + k)
     d = check_dense(gpu, qa, sa, qb, sb, label=f"default mid shape {m}x{n}x{k}")
     d2, _ = H.run_dense(qa, sa, qb, sb, gpu)
