@@ -146,10 +146,12 @@ const Config* configs(int* count) {
       make_config<256, 256, 2, 4, 2, dg::kDense, dg::kInterleaved, dg::kBf16>("bf16_256x256_w8_s2"),
       make_config<128, 128, 2, 2, 2, dg::kDense, dg::kInterleaved, dg::kBf16>("bf16_128x128_w4_s2"),
       make_config<64, 32, 2, 2, 4, dg::kDense, dg::kInterleaved, dg::kBf16>("bf16_64x32_w4_s4"),
+      make_config<64, 64, 1, 4, 3, dg::kDense, dg::kInterleaved, dg::kBf16>("bf16_64x64_w4_s3"),
       // FP4 (e2m1) dense (selected the same way by dtype)
       make_config<256, 256, 2, 4, 2, dg::kDense, dg::kInterleaved, dg::kFp4>("fp4_256x256_w8_s2"),
       make_config<128, 128, 2, 2, 2, dg::kDense, dg::kInterleaved, dg::kFp4>("fp4_128x128_w4_s2"),
       make_config<64, 32, 2, 2, 4, dg::kDense, dg::kInterleaved, dg::kFp4>("fp4_64x32_w4_s4"),
+      make_config<64, 64, 1, 4, 3, dg::kDense, dg::kInterleaved, dg::kFp4>("fp4_64x64_w4_s3"),
       // MoE FC1 + SwiGLU + FP8 requantisation, masked layout (a 256-column
       // tile = 128 gate + 128 up columns = one 128-wide block of h)
       make_config<256, 256, 2, 4, 2, dg::kMasked, dg::kPingPong, dg::kFp8, dg::kEpiSwigluFp8>("swiglu_256x256_w8_s2_pp"),
@@ -366,21 +368,24 @@ int dense_splits(const Config* c, int num_tiles, int kb_count, const DeviceInfo*
 // measurements are next to big_tiles_enough and in the config table).
 const Config* dense_default_config(int dtype, int m, int n, const DeviceInfo* info) {
   const bool mid = m <= 256 || n <= 256 || !big_tiles_enough(m, n, info);
+  // Few 128 x 128 tiles: smaller tiles (four or more workgroups per CU), or
+  // a third stage, keep more loads in flight per CU than split-K of the
+  // 128 x 128 tile alone does.
+  const long long t128 = (long long)((m + 127) / 128) * ((n + 127) / 128);
+  const bool few = mid && m <= 256 && t128 <= 64;
   switch (dtype) {
     case dg::kBf16:
-      if (m <= 64) return find_config("bf16_64x32_w4_s4", dg::kDense, dg::kBf16);
+      if (m <= 64 || (few && n <= 1024)) return find_config("bf16_64x32_w4_s4", dg::kDense, dg::kBf16);
+      if (few && n <= 4096) return find_config("bf16_64x64_w4_s3", dg::kDense, dg::kBf16);
       return find_config(mid ? "bf16_128x128_w4_s2" : "bf16_256x256_w8_s2", dg::kDense, dg::kBf16);
     case dg::kFp4:
-      if (m <= 64) return find_config("fp4_64x32_w4_s4", dg::kDense, dg::kFp4);
+      if (m <= 64 || (few && n <= 1024)) return find_config("fp4_64x32_w4_s4", dg::kDense, dg::kFp4);
+      if (few || (mid && t128 <= 72 && n >= 1024)) return find_config("fp4_64x64_w4_s3", dg::kDense, dg::kFp4);
       return find_config(mid ? "fp4_128x128_w4_s2" : "fp4_256x256_w8_s2", dg::kDense, dg::kFp4);
     default: {
       if (m <= 64) return find_config(n <= 4096 ? "dense_64x32_w4_s4" : "dense_64x64_w4_s3", dg::kDense);
       if (!mid) return find_config("dense_256x256_w8_s2", dg::kDense);
-      // Few 128 x 128 tiles: smaller tiles (four or more workgroups per CU),
-      // or a third stage, keep more loads in flight per CU than split-K of
-      // the 128 x 128 tile alone does.
-      const long long t128 = (long long)((m + 127) / 128) * ((n + 127) / 128);
-      if (m <= 256 && t128 <= 64) return find_config(n <= 1024 ? "dense_64x32_w4_s4" : "dense_64x64_w4_s3", dg::kDense);
+      if (few) return find_config(n <= 1024 ? "dense_64x32_w4_s4" : "dense_64x64_w4_s3", dg::kDense);
       if (t128 <= 72 && n >= 1024) return find_config("dense_128x128_w4_s3", dg::kDense);
       return find_config("dense_128x128_w4_s2", dg::kDense);
     }

@@ -25,7 +25,7 @@ from tests import gpu_harness as H
 
 pytestmark = pytest.mark.gpu
 
-FP4_CONFIGS = ["fp4_256x256_w8_s2", "fp4_128x128_w4_s2", "fp4_64x32_w4_s4"]
+FP4_CONFIGS = ["fp4_256x256_w8_s2", "fp4_128x128_w4_s2", "fp4_64x32_w4_s4", "fp4_64x64_w4_s3"]
 
 
 def with_ties(x):
@@ -83,7 +83,8 @@ def check_fp4(gpu, pa, sa, pb, sb, label):
 
 
 @pytest.mark.parametrize("m,n,k", [(128, 512, 1024), (1, 16, 256), (17, 40, 256), (200, 176, 512),
-                                   (64, 2112, 512), (300, 520, 768), (513, 257, 256)])
+                                   (64, 2112, 512), (300, 520, 768), (513, 257, 256), (200, 2112, 1024),
+                                   (384, 2112, 512)])
 def test_fp4_default_selection(gpu, m, n, k):
     check_fp4(gpu, *fp4_case(m, n, k, seed=m + n + k), label=f"fp4 {m}x{n}x{k}")
 

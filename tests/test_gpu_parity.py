@@ -325,8 +325,10 @@ def bf16_bits(x):
     return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("cfg", [None, "bf16_256x256_w8_s2", "bf16_128x128_w4_s2", "bf16_64x32_w4_s4"])
-@pytest.mark.parametrize("m,n,k", [(300, 520, 640), (64, 2112, 1024), (1, 16, 64), (520, 300, 128)])
+@pytest.mark.parametrize("cfg", [None, "bf16_256x256_w8_s2", "bf16_128x128_w4_s2", "bf16_64x32_w4_s4",
+                                 "bf16_64x64_w4_s3"])
+@pytest.mark.parametrize("m,n,k", [(300, 520, 640), (64, 2112, 1024), (1, 16, 64), (520, 300, 128),
+                                   (200, 2112, 512)])
 def test_bf16_gemm(gpu, cfg, m, n, k, monkeypatch):
     if cfg:
         monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
