@@ -130,6 +130,7 @@ const Config* configs(int* count) {
       make_config<128, 256, 1, 4, 3, dg::kContiguous>("contig_128x256_w4_s3"),
       make_config<128, 256, 1, 4, 2, dg::kContiguous, dg::kSingleB>("contig_128x256_w4_s2_sb"),
       make_config<128, 256, 1, 4, 2, dg::kContiguous>("contig_128x256_w4_s2"),
+      make_config<64, 64, 1, 4, 3, dg::kContiguous>("contig_64x64_w4_s3"),
       // masked
       make_config<256, 256, 2, 4, 2, dg::kMasked>("masked_256x256_w8_s2"),
       make_config<256, 256, 2, 4, 2, dg::kMasked, dg::kPingPong>("masked_256x256_w8_s2_pp"),
@@ -636,9 +637,17 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, cons
   if (int s = forced_config(dg::kContiguous, &c)) return s;
   if (!c) {
     // 128 x 256 tiles with one B buffer (two workgroups per CU) once there
-    // are enough of them to fill the GPU; 128 x 128 tiles below that
+    // are enough of them to fill the GPU; 128 x 128 tiles below that, and
+    // 64 x 64 tiles (more workgroups per CU) while 128 x 128 tiles would be
+    // at most 128: 4 x 128 rows, N 4096, K 7168 in 49.8 against 63.7 us,
+    // N 2112 in 42.9 against 59.9 us; at 256 such tiles they lose (101
+    // against 72 us).
     const long long tiles = (long long)(m / 128) * ((n + 255) / 256);
-    c = find_config(tiles >= info->cus ? "contig_128x256_w4_s2_sb" : "contig_128x128_w4_s2", dg::kContiguous);
+    const long long t128 = (long long)(m / 128) * ((n + 127) / 128);
+    c = find_config(t128 <= 128        ? "contig_64x64_w4_s3"
+                    : tiles >= info->cus ? "contig_128x256_w4_s2_sb"
+                                         : "contig_128x128_w4_s2",
+                    dg::kContiguous);
   }
   dg::GemmParams p{};
   p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.m_indices = m_indices;

@@ -363,17 +363,26 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   const int row_limit = p.m;  // rows that exist in memory (load clamp)
   int valid_rows = p.m;       // rows with a result (masked: the expert's count)
   if (VAR == kContiguous) {
+    // The tile's expert is the largest valid tag of its 128-row alignment
+    // block; a tile of fewer rows scans the whole block, so every tile of a
+    // block agrees on it.
+    constexpr int kBlk = BM < 128 ? 128 : BM;
+    static_assert(kThreads >= kBlk, "one row tag per thread");
+    const int blk0 = m0 & ~(kBlk - 1);
     if (threadIdx.x == 0) s_flag = -1;
     __syncthreads();
     int tag = -1;
-    if (threadIdx.x < BM) {
-      tag = p.m_indices[m0 + threadIdx.x];
+    if (threadIdx.x < kBlk) {
+      tag = p.m_indices[blk0 + threadIdx.x];
       if (tag >= 0 && tag < p.num_groups) atomicMax(&s_flag, tag);
     }
     __syncthreads();
     const int expert = s_flag;
     if (expert < 0) return;  // a block of padding rows only
-    if (threadIdx.x < BM) s_row_ok[threadIdx.x] = (tag == expert);
+    const int r = blk0 + (int)threadIdx.x - m0;  // this thread's row in the tile
+    const bool mine = threadIdx.x < kBlk && r >= 0 && r < BM;
+    if (mine) s_row_ok[r] = (tag == expert);
+    if (!__syncthreads_or(mine && tag == expert)) return;  // no row of this tile has a result
     B += (size_t)expert * p.n * p.k;
     SFB += (size_t)expert * p.nb_count * p.sk_count;
   } else if (VAR == kMasked) {

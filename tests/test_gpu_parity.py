@@ -85,7 +85,7 @@ def test_dense_unit_scale_exact_values(gpu):
 
 @pytest.mark.parametrize("cfg", [None, "contig_128x256_w8_s3", "contig_128x128_w4_s3", "contig_128x128_w4_s2",
                                  "contig_128x256_w8_s2", "contig_128x256_w4_s3", "contig_128x256_w4_s2",
-                                 "contig_128x256_w4_s2_sb"])
+                                 "contig_128x256_w4_s2_sb", "contig_64x64_w4_s3"])
 def test_contiguous(gpu, cfg, monkeypatch):
     if cfg:
         monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
@@ -106,6 +106,35 @@ def test_contiguous(gpu, cfg, monkeypatch):
     bits = H.d_bits(d)
     assert np.all(bits[~valid] == H.SENTINEL)
     assert H.guard_untouched(flat, d.numel())
+
+
+def test_contiguous_block_expert_same_for_64_row_tiles(gpu, monkeypatch):
+    # A 128-row block whose rows carry two valid tags (outside the alignment
+    # contract): its expert is the largest tag, and rows with another tag get
+    # no result.  A 64-row tile scans the whole block, so it must agree with
+    # the 128-row tile bit for bit.
+    group_rows = [128, 128, 256]
+    n, k = 320, 384
+    x = W.draw_contiguous(group_rows, n, k, seed=9)
+    idx = x["m_indices"].copy()
+    idx[64:128] = 1  # block 0: rows 0-63 tag 0, rows 64-127 tag 1 -> expert 1
+    qa, sa = oracle.quantize_a_1x128(x["a"])
+    qbs = [oracle.quantize_b_128x128(x["b"][g]) for g in range(len(group_rows))]
+    qb = np.stack([q for q, _ in qbs])
+    sb = np.stack([s for _, s in qbs])
+    out = {}
+    for cfg in ["contig_128x128_w4_s2", "contig_64x64_w4_s3"]:
+        monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+        print(f"[case] contiguous mixed block {cfg}", flush=True)
+        d, _ = H.run_contiguous(qa, sa, qb, sb, idx, gpu)
+        out[cfg] = H.d_bits(d)
+    assert np.array_equal(out["contig_128x128_w4_s2"], out["contig_64x64_w4_s3"])
+    bits = out["contig_64x64_w4_s3"]
+    assert np.all(bits[:64] == H.SENTINEL)  # tag 0 in a block whose expert is 1
+    r, valid = oracle.grouped_contiguous_ref(qa, sa, qb, sb, idx)
+    got = bits[64:].view(np.uint16).astype(np.uint32) << 16
+    res = oracle.tolerance_check(got.view(np.float32).astype(np.float64), r[64:], valid[64:, None])
+    assert res["ok"], res
 
 
 @pytest.mark.parametrize("cfg,max_m", [(None, 96), (None, 256), ("masked_256x128_w4_s2", 300),
