@@ -459,11 +459,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
     b_off[jj] = ((uint32_t)row * (uint32_t)K) | (16u * chunk);
     b_live += j < kJb ? 1 : 0;
   }
-  // Row scales: BM floats, one dword instruction per 64 rows.  Every wave
-  // issues exactly one (waves past the needed count repeat a block with the
-  // same data), so every wave issues the same number of loads per slab.
+  // Row scales: BM floats, one dword instruction per 64 rows, issued by
+  // waves 0 .. kSaInsts-1; the B block scales by the last wave.  Waves thus
+  // issue different numbers of loads per slab (c_loads): each waits for its
+  // own, and the barrier after those waits covers them all.
   constexpr int kSaInsts = (BM + 63) / 64;
-  const int sa_blk = wave % kSaInsts;
+  static_assert(kSaInsts <= kWaves, "one wave per 64 rows of row scales");
+  const bool sa_wave = wave < kSaInsts;
+  const bool sb_wave = wave == kWaves - 1;
+  const int sa_blk = sa_wave ? wave : 0;
   const bool sa_lane = sa_blk * 64 + lane < BM;
   uint32_t sa_off;
   {
@@ -471,7 +475,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
     row = row < row_limit ? row : row_limit - 1;
     sa_off = (uint32_t)row;
   }
-  // B block scales of the 128-row blocks this tile touches (every wave)
+  // B block scales of the 128-row blocks this tile touches
   // (SwiGLU: the gate block of the tile's h columns, then the up block)
   const int nb0 = n0 >> 7;
   const bool sb_lane = lane < (EPI == kEpiSwigluFp8 ? 2 : S::kSbCount);
@@ -481,9 +485,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
     blk = blk < p.nb_count ? blk : p.nb_count - 1;
     sb_off = (uint32_t)blk * (uint32_t)p.sk_count;  // sfb row stride: all K scale slabs
   }
-  // scale loads per slab: row and block scales of each of its scale slabs
-  constexpr int kScaleDma = DT == kBf16 ? 0 : 2 * kSps;  // bf16 operands carry no scales
-  const int c_loads = a_live + b_live + kScaleDma;
+  // scale load slots per slab: row and block scales of each of its scale
+  // slabs (bf16 operands carry no scales); a wave issues those it owns
+  constexpr int kScaleDma = DT == kBf16 ? 0 : 2 * kSps;
+  const int c_loads = a_live + b_live + (kScaleDma / 2) * ((sa_wave ? 1 : 0) + (sb_wave ? 1 : 0));
 
   // Buffer descriptors of this tile's operands (sizes in bytes; the host
   // keeps every operand below 4 GiB).
@@ -513,10 +518,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
       const int h = e >> 1;                 // scale slab of this slab
       const uint32_t ss = (uint32_t)(kb * kSps + h);
       if ((e & 1) == 0) {
-        if (sa_lane)
+        if (sa_wave && sa_lane)
           lds_dma4(rs_sa, sa_off * 4u, ss * (uint32_t)p.sfa_ld * 4u, st + S::kA + S::kB + h * BM * 4 + sa_blk * 256);
       } else {
-        if (sb_lane) lds_dma4(rs_sb, sb_off * 4u, ss * 4u, st + S::kA + S::kB + S::kSa + h * 256);
+        if (sb_wave && sb_lane) lds_dma4(rs_sb, sb_off * 4u, ss * 4u, st + S::kA + S::kB + S::kSa + h * 256);
       }
     }
   };
