@@ -158,22 +158,23 @@ __device__ __forceinline__ v4i_rsrc make_rsrc(const void* base, uint32_t bytes) 
 
 constexpr int kVmPerDma = 2;  // vmcnt events per lds_dma16 / lds_dma4: the EXEC = 0 load and the DMA
 
-// The EXEC = 0 load names the offset register as its destination: with no
-// lane active nothing is written.
-#define DG_M0_GUARD                                                              \
-  "s_mov_b64 %0, exec\n\ts_mov_b64 exec, 0\n\tbuffer_load_dword %1, %1, %2, 0 offen\n\t" \
-  "s_mov_b64 exec, %0\n\t"
+// The guard: s_and_saveexec saves EXEC and clears it (SCC is clobbered), the
+// EXEC = 0 load names the offset register as its destination (with no lane
+// active nothing is written), then M0 takes the new base and EXEC comes
+// back; the EXEC restore is also the one wait state the DMA needs after the
+// M0 write.
+#define DG_M0_GUARD "s_and_saveexec_b64 %0, 0\n\tbuffer_load_dword %1, %1, %2, 0 offen\n\t"
 
 __device__ __forceinline__ void lds_dma16(v4i_rsrc rs, uint32_t voff, uint32_t soff, void* lds_dst) {
   uint64_t exec_save;
-  asm volatile(DG_M0_GUARD "s_mov_b32 m0, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               : "=&s"(exec_save) : "v"(voff), "s"(rs), "s"(soff), "s"(lds_addr(lds_dst)) : "memory", "m0");
+  asm volatile(DG_M0_GUARD "s_mov_b32 m0, %4\n\ts_mov_b64 exec, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               : "=&s"(exec_save) : "v"(voff), "s"(rs), "s"(soff), "s"(lds_addr(lds_dst)) : "memory", "m0", "scc");
 }
 
 __device__ __forceinline__ void lds_dma4(v4i_rsrc rs, uint32_t voff, uint32_t soff, void* lds_dst) {
   uint64_t exec_save;
-  asm volatile(DG_M0_GUARD "s_mov_b32 m0, %4\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-               : "=&s"(exec_save) : "v"(voff), "s"(rs), "s"(soff), "s"(lds_addr(lds_dst)) : "memory", "m0");
+  asm volatile(DG_M0_GUARD "s_mov_b32 m0, %4\n\ts_mov_b64 exec, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               : "=&s"(exec_save) : "v"(voff), "s"(rs), "s"(soff), "s"(lds_addr(lds_dst)) : "memory", "m0", "scc");
 }
 #undef DG_M0_GUARD
 
