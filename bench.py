@@ -54,11 +54,12 @@ def parse():
                     help="'all', 'main', or a comma list of workload names for the extra figures")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--mode", choices=["bench", "counters"], default="bench",
+    ap.add_argument("--mode", choices=["bench", "counters", "oracle"], default="bench",
                     help="counters: run plain kernels of known traffic (1 GiB fill, 1 GiB read; "
                          "calibration for rocprofv3 FETCH_SIZE/WRITE_SIZE), then eager GEMM launches "
                          "of the headline workload and of the --workloads list ('main' = none), "
-                         "print nothing")
+                         "print nothing; oracle: time the CPU oracle's GEMM on the five configurations "
+                         "and print one JSON line")
     return ap.parse_args()
 
 
@@ -104,8 +105,73 @@ class Rotation:
         return self.sets[i % self.r]
 
 
+class ClockSampler:
+    """Samples the GPU's current shader (GFX) clock through amdsmi from a host
+    thread while kernels run; the samples taken during a timed region are its
+    SCLK record.  Empty when amdsmi is not available."""
+
+    def __init__(self):
+        self.handle = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if handles:
+                self.amdsmi = amdsmi
+                self.handle = handles[0]
+        except Exception:  # pragma: no cover - informational only
+            self.handle = None
+        self.samples = []
+        self._stop = None
+
+    def read_mhz(self):
+        if self.handle is None:
+            return None
+        try:
+            info = self.amdsmi.amdsmi_get_clock_info(self.handle, self.amdsmi.AmdSmiClkType.GFX)
+            v = info.get("clk", info.get("cur_clk"))
+            return float(v) if v is not None else None
+        except Exception:  # pragma: no cover
+            return None
+
+    def __enter__(self):
+        import threading
+        self.samples = []
+        if self.handle is None:
+            return self
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                v = self.read_mhz()
+                if v is not None:
+                    self.samples.append(v)
+                time.sleep(0.0005)
+
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._stop is not None:
+            self._stop.set()
+            self._thread.join()
+        return False
+
+    def summary(self):
+        if not self.samples:
+            return None
+        s = sorted(self.samples)
+        return {"samples": len(s), "median_mhz": s[len(s) // 2], "min_mhz": s[0], "max_mhz": s[-1]}
+
+
+CLOCK = None
+
+
 def kernel_time_us(torch, dg, launch, rot, n_launch, warm=20):
-    """Average duration of the GEMM kernel itself over n_launch launches."""
+    """Duration of the GEMM kernel itself over n_launch launches (events at
+    kernel start and end): average, median, p10, p90, and the shader clock
+    sampled meanwhile."""
     for i in range(warm):
         launch(rot[i])
     torch.cuda.synchronize()
@@ -114,12 +180,15 @@ def kernel_time_us(torch, dg, launch, rot, n_launch, warm=20):
     for e in starts + stops:
         e.record()  # materialise the underlying HIP events
     torch.cuda.synchronize()
-    for i in range(n_launch):
-        dg.profile_next_launch(starts[i], stops[i])
-        launch(rot[i])
-    torch.cuda.synchronize()
+    with CLOCK:
+        for i in range(n_launch):
+            dg.profile_next_launch(starts[i], stops[i])
+            launch(rot[warm + i])
+        torch.cuda.synchronize()
     times = sorted(starts[i].elapsed_time(stops[i]) * 1e3 for i in range(n_launch))
-    return sum(times) / len(times), times[len(times) // 2]
+    pct = lambda q: times[min(len(times) - 1, int(q * len(times)))]
+    return {"avg": sum(times) / len(times), "median": pct(0.5), "p10": pct(0.1), "p90": pct(0.9),
+            "sclk": CLOCK.summary()}
 
 
 def setup_workload(torch, np, dg, W, name, dev):
@@ -272,46 +341,135 @@ def setup_workload(torch, np, dg, W, name, dev):
     return w.kind, dict(masked_m=inp["masked_m"], max_m=max_m, n=n, k=k), rot, launch, None, inp
 
 
-def cpu_oracle_baseline(np, W, inp, m, n, k, seconds):
-    """Time the oracle doing the main step (quantise A, GEMM) on the host."""
-    import oracle
+def host_info():
+    """CPU model, the cores this process may run on, and NumPy's BLAS."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    cores = len(os.sched_getaffinity(0))
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+        infos = [t for t in threadpool_info() if t.get("user_api") == "blas"]
+        if infos:
+            blas = f"{infos[0].get('internal_api')} {infos[0].get('version')}"
     except Exception:  # pragma: no cover - informational only
-        threads = 1
+        pass
+    return model, cores, blas
+
+
+def blas_threads(cores):
+    """Context that runs NumPy's BLAS on `cores` threads (no-op without threadpoolctl)."""
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=cores, user_api="blas")
+    except Exception:  # pragma: no cover
+        import contextlib
+        return contextlib.nullcontext()
+
+
+def cpu_oracle_baseline(np, W, inp, m, n, k, seconds):
+    """Time the oracle doing the main step (quantise A, GEMM) on the host, on
+    every core of this process's affinity set."""
+    import oracle
+    model, cores, blas = host_info()
     qb, sb = oracle.quantize_b_128x128(inp["b"])  # weights: outside the timed loop
     flops, gemm_bytes = W.algorithmic_work("dense", m=m, n=n, k=k)
     step_bytes = gemm_bytes + m * k * 4 + m * k + 4 * m * (k // 128)
-    t0 = time.perf_counter()
-    iters = 0
-    while True:
-        qa, sa = oracle.quantize_a_1x128(inp["a"])
-        oracle.gemm_nt_ref(qa, sa, qb, sb)
-        iters += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": step_bytes * iters / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+    with blas_threads(cores):
+        t0 = time.perf_counter()
+        iters = 0
+        while True:
+            qa, sa = oracle.quantize_a_1x128(inp["a"])
+            oracle.gemm_nt_ref(qa, sa, qb, sb)
+            iters += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    return {"value": step_bytes * iters / el / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "cpu": model, "blas": blas,
             "sample": f"the whole decode step (quantise A 64x7168, fp64 GEMM 64x2112x7168) "
                       f"x{iters} in {el:.1f} s; {flops * iters / el / 1e9:.2f} GFLOP/s"}
 
 
+ORACLE_CONFIGS = ["dense_128x512x1024", "dense_decode_64x2112x7168", "dense_large_4096x7168x16384",
+                  "moe_contiguous_4x8192_n4096_k7168", "moe_masked_16x256_n4096_k7168"]
+
+
+def oracle_timing(np, W):
+    """The oracle's GEMM on each of the five configurations, on the host's
+    cores: the two large ones once, the others best of three.  Inputs are the
+    workloads' seeded draws, quantised by the oracle outside the timing."""
+    import oracle
+    model, cores, blas = host_info()
+    rows = []
+    for name in ORACLE_CONFIGS:
+        w = W.WORKLOADS[name]
+        inp = W.draw(name)
+        if w.kind == "dense":
+            qa, sa = oracle.quantize_a_1x128(inp["a"])
+            qb, sb = oracle.quantize_b_128x128(inp["b"])
+            run = lambda: oracle.gemm_nt_ref(qa, sa, qb, sb)
+        elif w.kind == "contiguous":
+            qa, sa = oracle.quantize_a_1x128(inp["a"])
+            qbs = [oracle.quantize_b_128x128(inp["b"][g]) for g in range(inp["b"].shape[0])]
+            qb = np.stack([q for q, _ in qbs])
+            sb = np.stack([s for _, s in qbs])
+            run = lambda: oracle.grouped_contiguous_ref(qa, sa, qb, sb, inp["m_indices"])
+        else:
+            g = inp["a"].shape[0]
+            qas = [oracle.quantize_a_1x128(inp["a"][i]) for i in range(g)]
+            qbs = [oracle.quantize_b_128x128(inp["b"][i]) for i in range(g)]
+            qa = np.stack([q for q, _ in qas])
+            sa = np.stack([s for _, s in qas])
+            qb = np.stack([q for q, _ in qbs])
+            sb = np.stack([s for _, s in qbs])
+            run = lambda: oracle.grouped_masked_ref(qa, sa, qb, sb, inp["masked_m"])
+        reps = 1 if name in ("dense_large_4096x7168x16384", "moe_contiguous_4x8192_n4096_k7168") else 3
+        best = None
+        with blas_threads(cores):
+            for _ in range(reps):
+                t0 = time.perf_counter()
+                run()
+                el = time.perf_counter() - t0
+                best = el if best is None else min(best, el)
+        fl, by = W.workload_work(name, inp)
+        rows.append({"workload": name, "seconds": round(best, 3), "reps": reps,
+                     "gflops": round(fl / best / 1e9, 2), "gbs": round(by / best / 1e9, 3)})
+        print(f"[oracle] {name}: {best:.3f} s (best of {reps}), {fl / best / 1e9:.2f} GFLOP/s",
+              file=sys.stderr, flush=True)
+        del inp
+    return {"cpu": model, "cores": cores, "blas": blas, "configs": rows}
+
+
 def main():
+    global CLOCK
     args = parse()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         return 2
     import numpy as np
+
+    import workloads as W
+    if args.mode == "oracle":
+        print(json.dumps({"oracle_cpu_timing": oracle_timing(np, W)}))
+        return 0
+
     import torch
 
     import fp8_block_scaled_nt_amd as dg
-    import workloads as W
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
+    CLOCK = ClockSampler()
 
     # ---- headline step: quantise A + GEMM on the decode shape
     kind, params, rot, launch, quant, inp = setup_workload(torch, np, dg, W, MAIN_WORKLOAD, dev)
@@ -356,33 +514,42 @@ def main():
         step(i)
     torch.cuda.synchronize()
     stream = torch.cuda.Stream()
+    # the split-K workspace of the capture stream, sized before capture
+    dg.reserve_workspace(dg.dense_workspace_size(m, n, k), stream)
     g_warm = torch.cuda.CUDAGraph()
     g_main = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
         with torch.cuda.graph(g_warm, stream=stream):
             for i in range(args.warmup):
                 step(i)
+        # the timed steps continue the rotation after the warm-up's sets, so
+        # no timed step finds its operands where a warm-up step left them
         with torch.cuda.graph(g_main, stream=stream):
             for i in range(args.steps):
-                step(i)
+                step(args.warmup + i)
     torch.cuda.synchronize()
     g_warm.replay()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    g_main.replay()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with CLOCK:
+        t0 = time.perf_counter()
+        g_main.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    step_clock = CLOCK.summary()
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes * args.steps / wall / 1e9
 
     # ---- the GEMM kernel alone, timed at the kernel
-    avg_us, med_us = kernel_time_us(torch, dg, launch, rot, args.kernel_launches)
+    kt = kernel_time_us(torch, dg, launch, rot, args.kernel_launches)
+    avg_us = kt["avg"]
     achieved = gemm_bytes / (avg_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(MAIN_WORKLOAD),
-                "kernel": "gemm_fp8_nt_kernel (dense)", "kernel_avg_us": round(avg_us, 3),
-                "kernel_median_us": round(med_us, 3), "algorithmic_bytes": gemm_bytes}
+                "kernel": "gemm_fp8_nt_kernel<64, 32, 2, 2, 4> (dense fp8, 64 x 32 tiles, split-K 7)",
+                "kernel_avg_us": round(avg_us, 3), "kernel_median_us": round(kt["median"], 3),
+                "kernel_p10_us": round(kt["p10"], 3), "kernel_p90_us": round(kt["p90"], 3),
+                "launches": args.kernel_launches, "sclk": kt["sclk"], "algorithmic_bytes": gemm_bytes}
 
     # ---- other workloads: GEMM kernel figures
     extra = {}
@@ -393,17 +560,21 @@ def main():
     for name in names:
         kind_x, p_x, rot_x, launch_x, _, inp_x = setup_workload(torch, np, dg, W, name, dev)
         fl, by = W.algorithmic_work(kind_x, **p_x)
-        a_us, md_us = kernel_time_us(torch, dg, launch_x, rot_x, max(10, args.kernel_launches // 4))
+        kx = kernel_time_us(torch, dg, launch_x, rot_x, max(10, args.kernel_launches // 4))
+        a_us = kx["avg"]
         tf = fl / (a_us * 1e-6) / 1e12
         gbs = by / (a_us * 1e-6) / 1e9
         peak_tf = {"bf16": BF16_PEAK_TFLOPS, "fp4": FP4_PEAK_TFLOPS}.get(kind_x, FP8_PEAK_TFLOPS)
         bound = "mfma" if fl / by > peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
-        extra[name] = {"kernel_avg_us": round(a_us, 2), "kernel_median_us": round(md_us, 2),
+        extra[name] = {"kernel_avg_us": round(a_us, 2), "kernel_median_us": round(kx["median"], 2),
+                       "kernel_p10_us": round(kx["p10"], 2), "kernel_p90_us": round(kx["p90"], 2),
                        "tflops": round(tf, 1), "gbs": round(gbs, 1), "bound": bound,
                        "peak": peak_tf if bound == "mfma" else HBM_PEAK_GBS,
                        "frac": round(tf / peak_tf if bound == "mfma" else gbs / HBM_PEAK_GBS, 4),
+                       "sclk": kx["sclk"],
                        "algorithmic_flops": fl, "algorithmic_bytes": by, "traffic": measured_traffic(name)}
-        print(f"[bench] {name}: {a_us:.1f} us, {tf:.1f} TFLOP/s, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+        print(f"[bench] {name}: {a_us:.1f} us, {tf:.1f} TFLOP/s, {gbs:.0f} GB/s, sclk {kx['sclk']}",
+              file=sys.stderr, flush=True)
         del rot_x, inp_x
         torch.cuda.empty_cache()
 
@@ -427,7 +598,8 @@ def main():
         "config": {"workload": MAIN_WORKLOAD, "m": m, "n": n, "k": k,
                    "step": "quantise A 1x128 + FP8 NT GEMM (B quantised 128x128 once)",
                    "step_algorithmic_bytes": step_bytes, "gemm_algorithmic_flops": flops,
-                   "rotation_sets": "operand copies > 512 MiB, one per step", "graph": True,
+                   "rotation_sets": "operand copies > 512 MiB, one per step; timed steps continue after the "
+                                    "warm-up's sets", "graph": True, "step_sclk": step_clock,
                    "gpu": props.name, "cus": props.multi_processor_count},
         "roofline": roofline,
         "cpu_baseline": cpu,

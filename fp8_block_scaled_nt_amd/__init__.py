@@ -23,7 +23,9 @@ import os
 import torch
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG_DIR, "libdg.so")
+# DG_LIBRARY names another build of the same library (e.g. one whose host
+# code is compiled with sanitizers); by default the in-tree libdg.so
+LIB_PATH = os.environ.get("DG_LIBRARY") or os.path.join(_PKG_DIR, "libdg.so")
 
 __all__ = [
     "DGError", "lib", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous",
@@ -62,7 +64,7 @@ _SIGNATURES = {
     "dg_last_error_message": [],
     "dg_version": [],
     "dg_profile_next_launch": [_vp, _vp],
-    "dg_reserve_workspace": [ctypes.c_size_t],
+    "dg_reserve_workspace": [ctypes.c_size_t, _vp],
     "dg_dense_workspace_size": [_ci, _ci, _ci, _ci, ctypes.POINTER(ctypes.c_size_t)],
 }
 _RESTYPES = {"dg_status_string": ctypes.c_char_p, "dg_last_error_message": ctypes.c_char_p,
@@ -121,9 +123,12 @@ def profile_next_launch(start_event, stop_event):
     _check(lib().dg_profile_next_launch(start_event._as_parameter_, stop_event._as_parameter_))
 
 
-def reserve_workspace(nbytes):
-    """Pre-allocate the split-K workspace on the current device."""
-    _check(lib().dg_reserve_workspace(int(nbytes)))
+def reserve_workspace(nbytes, stream=None):
+    """Size the split-K workspace of a stream (default: the current one) on
+    the current device for `nbytes` of partial tiles, so that later calls on
+    that stream allocate nothing (and can be captured in a graph)."""
+    st = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream()
+    _check(lib().dg_reserve_workspace(int(nbytes), st))
 
 
 _DTYPES = {"fp8": 0, "bf16": 1, "fp4": 2}

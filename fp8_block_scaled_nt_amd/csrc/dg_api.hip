@@ -18,9 +18,12 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <unordered_map>
+#include <vector>
 
 #include "gemm_kernel.h"
 #include "quant_kernel.h"
+#include "skinny_kernel.h"
 
 namespace {
 
@@ -67,13 +70,11 @@ DeviceInfo g_dev[kMaxDevices];
 std::once_flag g_dev_once[kMaxDevices];
 
 int current_device(int* dev, DeviceInfo** info) {
-  int count = 0;
-  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+  // hipGetDevice is a thread-local read; it fails when no device is visible
+  if (hipGetDevice(dev) != hipSuccess || *dev < 0 || *dev >= kMaxDevices) {
     (void)hipGetLastError();
     return fail(DG_ERR_NO_DEVICE, "no HIP device is visible");
   }
-  if (hipGetDevice(dev) != hipSuccess || *dev < 0 || *dev >= kMaxDevices)
-    return fail(DG_ERR_NO_DEVICE, "hipGetDevice failed");
   const int d = *dev;
   std::call_once(g_dev_once[d], [d]() {
     hipDeviceProp_t prop;
@@ -110,6 +111,8 @@ const Config* configs(int* count) {
       make_config<256, 256, 2, 4, 2, dg::kDense, dg::kPingPong>("dense_256x256_w8_s2_pp"),
       make_config<128, 256, 1, 4, 2, dg::kDense, dg::kSingleB>("dense_128x256_w4_s2_sb"),
       make_config<256, 224, 4, 2, 2, dg::kDense>("dense_256x224_w8_s2"),
+      make_config<128, 224, 2, 2, 2, dg::kDense, dg::kSingleB>("dense_128x224_w4_s2_sb"),
+      make_config<128, 224, 2, 2, 2, dg::kDense>("dense_128x224_w4_s2"),
       make_config<128, 256, 1, 4, 3, dg::kDense>("dense_128x256_w4_s3_wide"),
       make_config<256, 128, 4, 2, 3, dg::kDense>("dense_256x128_w8_s3"),
       make_config<256, 128, 2, 2, 2, dg::kDense>("dense_256x128_w4_s2"),
@@ -173,6 +176,51 @@ const Config* find_config(const char* name, int variant, int dtype = dg::kFp8, i
   return nullptr;
 }
 
+// ---- skinny-M fp8 configurations (dense calls with m <= 64): stream-K
+// runs of (tile, K slab) units, one unit per wave (skinny_kernel.h)
+struct SkinnyConfig {
+  const char* name;
+  int bn, nw, upw;
+  bool sa, sb;  // A / B staged through LDS (whole-row loads) or loaded in the MFMA layout
+  const void* fn;
+  int threads() const { return nw * 64; }
+  // per-wave staging of one unit's rows, later the per-wave fp32 accumulators
+  int smem() const {
+    const int stage = nw * ((sa ? 64 : 0) + (sb ? bn : 0)) * 128;
+    const int red = nw * upw * (64 * bn / 256) * 1024;
+    return stage > red ? stage : red;
+  }
+  int units_per_wg() const { return nw * upw; }
+};
+
+template <int BN, int NW, int UPW, bool SA, bool SB>
+SkinnyConfig make_skinny(const char* name) {
+  return SkinnyConfig{name, BN, NW, UPW, SA, SB,
+                      reinterpret_cast<const void*>(&dg::gemm_skinny_kernel<BN, NW, UPW, SA, SB>)};
+}
+
+const SkinnyConfig* skinny_configs(int* count) {
+  static const SkinnyConfig table[] = {
+      make_skinny<32, 16, 1, false, false>("skinny_64x32_w16_direct"),
+      make_skinny<32, 16, 1, true, false>("skinny_64x32_w16_stagea"),
+      make_skinny<32, 8, 2, true, true>("skinny_64x32_w8_u2_stage"),
+      make_skinny<32, 8, 2, false, false>("skinny_64x32_w8_u2_direct"),
+      make_skinny<32, 12, 1, true, true>("skinny_64x32_w12_stage"),
+      make_skinny<16, 16, 1, false, false>("skinny_64x16_w16_direct"),
+      make_skinny<64, 8, 1, true, false>("skinny_64x64_w8_stagea"),
+  };
+  *count = sizeof(table) / sizeof(table[0]);
+  return table;
+}
+
+const SkinnyConfig* find_skinny(const char* name) {
+  int cnt = 0;
+  const SkinnyConfig* t = skinny_configs(&cnt);
+  for (int i = 0; i < cnt; ++i)
+    if (strcmp(t[i].name, name) == 0) return &t[i];
+  return nullptr;
+}
+
 // DG_FORCE_CONFIG=<name> pins the configuration of the variant it names (for
 // tuning sweeps); an unknown name is an error rather than silently ignored.
 int forced_config(int variant, const Config** out, int dtype = dg::kFp8, int epi = dg::kEpiBf16) {
@@ -183,6 +231,7 @@ int forced_config(int variant, const Config** out, int dtype = dg::kFp8, int epi
   const Config* t = configs(&cnt);
   bool known = false;
   for (int i = 0; i < cnt; ++i) known = known || strcmp(t[i].name, e) == 0;
+  known = known || find_skinny(e) != nullptr;
   if (!known) return fail(DG_ERR_INVALID_ARGUMENT, "DG_FORCE_CONFIG names no configuration: %s", e);
   *out = find_config(e, variant, dtype, epi);
   return DG_OK;
@@ -194,6 +243,12 @@ constexpr int kMaxConfigs = 64;
 int g_per_cu[kMaxConfigs];  // resident workgroups per CU of each configuration (0: not known)
 
 void set_kernel_attributes() {
+  int scnt = 0;
+  const SkinnyConfig* st = skinny_configs(&scnt);
+  for (int i = 0; i < scnt; ++i) {
+    hipError_t e = hipFuncSetAttribute(st[i].fn, hipFuncAttributeMaxDynamicSharedMemorySize, st[i].smem());
+    if (e != hipSuccess) g_attr_err = e;
+  }
   int cnt = 0;
   const Config* t = configs(&cnt);
   for (int i = 0; i < cnt; ++i) {
@@ -227,39 +282,91 @@ int per_cu(const Config* c) {
   return (i >= 0 && i < kMaxConfigs && g_per_cu[i] > 0) ? g_per_cu[i] : 1;
 }
 
-// ---- split-K workspace: library-owned device memory per device, grown on
-// demand.  Layout: kCounterInts arrival counters (zeroed once, reset by the
-// kernels), then the fp32 partial tiles.
+// ---- split-K workspace: library-owned device memory, one block per
+// (device, stream).  Calls on one stream run in stream order, so they can
+// share a block; calls on different streams get different blocks and never
+// share an arrival counter or a partial tile.  Layout of a block:
+// kCounterInts arrival counters (reset by the kernels after use), then the
+// partial tiles; the whole block is zeroed when it is made.
+//
+// A block only grows: the larger block replaces it for later calls on that
+// stream, and the old one is retired, never freed, because a launch still in
+// flight or a captured graph may use it.  Growing costs a hipMalloc and a
+// zero-fill kernel on the calling stream (stream-ordered: no device-wide
+// synchronisation).  A call that would grow the block while its stream is
+// capturing a graph returns DG_ERR_WORKSPACE instead (dg_reserve_workspace
+// sizes the block beforehand).
 constexpr size_t kCounterInts = 1 << 16;
-struct Workspace {
-  std::mutex mu;
+struct StreamWorkspace {
   char* base = nullptr;
   size_t bytes = 0;
 };
-Workspace g_ws[kMaxDevices];
+struct DeviceWorkspaces {
+  std::mutex mu;
+  std::unordered_map<hipStream_t, StreamWorkspace> by_stream;
+  std::vector<void*> retired;  // kept until the process ends
+};
+DeviceWorkspaces g_ws[kMaxDevices];
 
-int ensure_workspace(int dev, size_t partial_bytes, float** partial, int** counters) {
-  Workspace& w = g_ws[dev];
+__global__ void zero_ints_kernel(int* p, long long n) {
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+constexpr size_t kWsHeader = kCounterInts * sizeof(int);  // the counters
+
+int ensure_workspace(int dev, hipStream_t stream, size_t partial_bytes, char** base) {
+  DeviceWorkspaces& w = g_ws[dev];
   std::lock_guard<std::mutex> lock(w.mu);
-  const size_t need = kCounterInts * sizeof(int) + partial_bytes;
-  if (w.bytes < need) {
-    if (w.base) {
-      hipError_t e = hipFree(w.base);  // synchronises the device
-      w.base = nullptr;
-      w.bytes = 0;
-      if (e != hipSuccess) return fail(DG_ERR_HIP, "hipFree(workspace): %s", hipGetErrorString(e));
+  StreamWorkspace& ws = w.by_stream[stream];
+  const size_t need = kWsHeader + partial_bytes;
+  if (ws.bytes < need) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(stream, &cap);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(DG_ERR_WORKSPACE, "the split-K workspace of this stream must grow to %zu bytes, and the stream's "
+                  "capture state cannot be queried (%s)", need, hipGetErrorString(e));
     }
-    size_t alloc = need < ((size_t)16 << 20) ? ((size_t)16 << 20) : need;
+    if (cap != hipStreamCaptureStatusNone)
+      return fail(DG_ERR_WORKSPACE, "the split-K workspace of this stream must grow to %zu bytes (it has %zu) while "
+                  "the stream is capturing; reserve it first with dg_reserve_workspace", need, ws.bytes);
+    size_t alloc = 2 * ws.bytes;
+    if (alloc < need) alloc = need;
+    if (alloc < ((size_t)4 << 20)) alloc = (size_t)4 << 20;
     void* ptr = nullptr;
-    hipError_t e = hipMalloc(&ptr, alloc);
-    if (e != hipSuccess) return fail(DG_ERR_HIP, "hipMalloc(workspace %zu): %s", alloc, hipGetErrorString(e));
-    e = hipMemset(ptr, 0, kCounterInts * sizeof(int));
-    if (e != hipSuccess) return fail(DG_ERR_HIP, "hipMemset(workspace): %s", hipGetErrorString(e));
-    w.base = (char*)ptr;
-    w.bytes = alloc;
+    e = hipMalloc(&ptr, alloc);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(DG_ERR_HIP, "hipMalloc(workspace %zu): %s", alloc, hipGetErrorString(e));
+    }
+    const long long words = (long long)(alloc / sizeof(int));
+    hipLaunchKernelGGL(zero_ints_kernel, dim3(1024), dim3(256), 0, stream, (int*)ptr, words);
+    e = hipGetLastError();
+    if (e != hipSuccess) {
+      w.retired.push_back(ptr);
+      return fail(DG_ERR_HIP, "workspace zero-fill launch failed: %s", hipGetErrorString(e));
+    }
+    if (ws.base) w.retired.push_back(ws.base);
+    ws.base = (char*)ptr;
+    ws.bytes = alloc;
   }
-  *counters = (int*)w.base;
-  *partial = (float*)(w.base + kCounterInts * sizeof(int));
+  *base = ws.base;
+  return DG_OK;
+}
+
+// Where a split-K call's counters and partial tiles live: the calling
+// stream's workspace block.
+struct WsView {
+  int* counters = nullptr;
+  char* partial = nullptr;
+};
+
+int get_workspace(int dev, hipStream_t stream, size_t partial_bytes, WsView* v) {
+  char* base = nullptr;
+  if (int s = ensure_workspace(dev, stream, partial_bytes, &base)) return s;
+  v->counters = (int*)base;
+  v->partial = base + kWsHeader;
   return DG_OK;
 }
 
@@ -421,9 +528,112 @@ int launch_dense(const Config* c, dg::GemmParams& p, int dev, const DeviceInfo* 
     if ((long long)p.num_tiles * p.splits > 0x7FFFFFFFLL)
       return fail(DG_ERR_UNSUPPORTED_SHAPE, "split-K grid too large (%d x %d)", p.num_tiles, p.splits);
     const size_t part = (size_t)p.num_tiles * p.splits * c->bm * c->bn * sizeof(float);
-    if (int s = ensure_workspace(dev, part, &p.ws_partial, &p.ws_count)) return s;
+    WsView v;
+    if (int s = get_workspace(dev, (hipStream_t)stream, part, &v)) return s;
+    p.ws_partial = (float*)v.partial;
+    p.ws_count = v.counters;
   }
   return launch(*c, p, p.num_tiles * p.splits, (hipStream_t)stream);
+}
+
+// ---- skinny-M plan: the stream-K partition of a dense fp8 call with m <= 64
+struct SkinnyPlan {
+  const SkinnyConfig* c = nullptr;
+  int tiles_n = 0, grid = 0, per = 0, rem = 0, max_contrib = 0;
+  size_t ws_bytes = 0;  // 0: no tile is cut between workgroups
+};
+
+// Workgroups: one per CU when there are enough units (a unit is one 128-wide
+// K slab of one 64 x BN tile), each taking an equal contiguous run of at most
+// NW units (one per wave); more workgroups when the runs would be longer than
+// NW.  A tile cut by run boundaries is added up by its last contributor, which
+// reads at most dg::kSkinnyMaxContrib partials, so runs are at least
+// ceil(KB / (dg::kSkinnyMaxContrib - 1)) units.  Returns false when the shape
+// does not fit these rules.
+bool skinny_plan(const SkinnyConfig* c, int m, int n, int kb, const DeviceInfo* info, SkinnyPlan* out) {
+  if (m < 1 || m > 64) return false;
+  const long long tiles_n = (n + c->bn - 1) / c->bn;
+  const long long units = tiles_n * kb;
+  if (units > (1LL << 30) || tiles_n > (long long)kCounterInts) return false;
+  long long grid = units < info->cus ? units : info->cus;
+  const long long need = (units + c->units_per_wg() - 1) / c->units_per_wg();  // runs of at most NW * UPW units
+  if (grid < need) grid = need;
+  const long long per_min = (kb + dg::kSkinnyMaxContrib - 2) / (dg::kSkinnyMaxContrib - 1);
+  if (per_min > c->units_per_wg()) return false;
+  if (grid > units / per_min) grid = units / per_min;
+  if (grid < need || grid < 1) return false;
+  SkinnyPlan pl;
+  pl.c = c;
+  pl.tiles_n = (int)tiles_n;
+  pl.grid = (int)grid;
+  pl.per = (int)(units / grid);
+  pl.rem = (int)(units % grid);
+  const int mc = (kb + pl.per - 1) / pl.per + 1;
+  pl.max_contrib = mc < dg::kSkinnyMaxContrib ? mc : dg::kSkinnyMaxContrib;
+  bool cut = false;
+  for (int L = 1; L < pl.grid && !cut; ++L) cut = ((long long)L * pl.per + (L < pl.rem ? L : pl.rem)) % kb != 0;
+  pl.ws_bytes = cut ? (size_t)tiles_n * pl.max_contrib * 64 * c->bn * sizeof(float) : 0;
+  *out = pl;
+  return true;
+}
+
+// The skinny configuration a dense fp8 call uses (nullptr: the tiled kernels):
+// DG_FORCE_CONFIG when it names a skinny configuration (then m must be at
+// most 64), else skinny_64x32_w16_stagea for m <= 16 while one run of units
+// per CU covers the shape.  Measured on N 2112, K 7168 (kernel time with
+// events, median): m 1, 8, 16: 10.1-10.4 against 11.1-11.3 us for the
+// tiled split-K kernel; m 32: level (11.0); m 48 and 64: 11.6 and 12.1
+// against 11.0 and 10.8 us, where reloading A in every run costs more than
+// the tiled kernel's pipelined LDS staging.
+int skinny_config(int m, int n, int kb, const DeviceInfo* info, SkinnyPlan* plan) {
+  plan->c = nullptr;
+  const char* e = getenv("DG_FORCE_CONFIG");
+  if (e && *e) {
+    const SkinnyConfig* c = find_skinny(e);
+    if (!c) return DG_OK;  // a tiled configuration (or an unknown name, reported by dense_config)
+    if (!skinny_plan(c, m, n, kb, info, plan))
+      return fail(DG_ERR_INVALID_ARGUMENT, "configuration %s does not take m=%d n=%d k=%d", e, m, n, kb * 128);
+    return DG_OK;
+  }
+  SkinnyPlan pl;
+  if (m <= 16 && skinny_plan(find_skinny("skinny_64x32_w16_stagea"), m, n, kb, info, &pl) && pl.grid <= info->cus)
+    *plan = pl;
+  return DG_OK;
+}
+
+int launch_skinny(const SkinnyPlan& pl, const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                  uint16_t* d, int m, int n, int k, int dev, dg_stream_t stream) {
+  if (int s = ensure_kernel_attributes()) return s;
+  dg::SkinnyParams p{};
+  p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d;
+  p.m = m; p.n = n; p.k = k;
+  p.kb_count = k / 128;
+  p.sfa_ld = sfa_ld(m);
+  p.tiles_n = pl.tiles_n;
+  p.per = pl.per;
+  p.rem = pl.rem;
+  p.max_contrib = pl.max_contrib;
+  if (pl.ws_bytes > 0) {
+    WsView v;
+    if (int s = get_workspace(dev, (hipStream_t)stream, pl.ws_bytes, &v)) return s;
+    p.ws_partial = (float*)v.partial;
+    p.ws_count = v.counters;
+  }
+  const SkinnyConfig& c = *pl.c;
+  if (log_enabled())
+    fprintf(stderr, "[dg] %s m=%d n=%d k=%d grid=%d threads=%d smem=%d per=%d rem=%d contrib=%d ws=%zu\n", c.name, m,
+            n, k, pl.grid, c.threads(), c.smem(), pl.per, pl.rem, pl.max_contrib, pl.ws_bytes);
+  void* args[] = {&p};
+  hipError_t e;
+  if (g_prof_start || g_prof_stop) {
+    e = hipExtLaunchKernel(c.fn, dim3(pl.grid), dim3(c.threads()), args, c.smem(), (hipStream_t)stream,
+                           g_prof_start, g_prof_stop, 0);
+    g_prof_start = g_prof_stop = nullptr;
+  } else {
+    e = hipLaunchKernel(c.fn, dim3(pl.grid), dim3(c.threads()), args, c.smem(), (hipStream_t)stream);
+  }
+  if (e != hipSuccess) return fail(DG_ERR_HIP, "launch of %s failed: %s", c.name, hipGetErrorString(e));
+  return ok();
 }
 
 int quantize_a(const void* kernel, const float* x, uint8_t* q, float* sfa, int m, int k, dg_stream_t stream) {
@@ -467,6 +677,29 @@ int quantize_b(const void* kernel, const float* x, uint8_t* q, float* sfb, int n
 }
 
 
+// The dense fp8 call.
+int fp8_gemm(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb, uint16_t* d, int m, int n, int k,
+             dg_stream_t stream) {
+  if (!a || !sfa || !b || !sfb || !d) return fail(DG_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (m < 0) return fail(DG_ERR_INVALID_ARGUMENT, "m must be >= 0 (got %d)", m);
+  if (int s = check_k_n(n, k)) return s;
+  if (int s = check_rows(m, k)) return s;
+  if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d))
+    return fail(DG_ERR_MISALIGNED, "pointers must be 16-byte aligned");
+  if (m == 0) return ok();
+  int dev;
+  DeviceInfo* info;
+  if (int s = current_device(&dev, &info)) return s;
+  SkinnyPlan sp;
+  if (int s = skinny_config(m, n, k / 128, info, &sp)) return s;
+  if (sp.c) return launch_skinny(sp, a, sfa, b, sfb, d, m, n, k, dev, stream);
+  const Config* c;
+  if (int s = dense_config(dg::kFp8, m, n, info, &c)) return s;
+  dg::GemmParams p{};
+  p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d;
+  return launch_dense(c, p, dev, info, m, n, k, k / 128, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -481,13 +714,12 @@ static_assert((int)DG_DTYPE_FP8 == (int)dg::kFp8 && (int)DG_DTYPE_BF16 == (int)d
 
 const char* dg_version(void) { return "dg-gfx950 0.1"; }
 
-int dg_reserve_workspace(size_t bytes) {
+int dg_reserve_workspace(size_t bytes, dg_stream_t stream) {
   int dev;
   DeviceInfo* info;
   if (int s = current_device(&dev, &info)) return s;
-  float* part;
-  int* cnt;
-  if (int s = ensure_workspace(dev, bytes, &part, &cnt)) return s;
+  char* base;
+  if (int s = ensure_workspace(dev, (hipStream_t)stream, bytes, &base)) return s;
   return ok();
 }
 
@@ -521,6 +753,14 @@ int dg_dense_workspace_size(int dtype, int m, int n, int k, size_t* bytes) {
   DeviceInfo* info;
   if (int s = current_device(&dev, &info)) return s;
   if (int s = ensure_kernel_attributes()) return s;
+  if (dtype == DG_DTYPE_FP8) {
+    SkinnyPlan sp;
+    if (int s = skinny_config(m, n, k / 128, info, &sp)) return s;
+    if (sp.c) {
+      *bytes = sp.ws_bytes;
+      return ok();
+    }
+  }
   const Config* c;
   if (int s = dense_config(dtype, m, n, info, &c)) return s;
   const long long tiles = (long long)((m + c->bm - 1) / c->bm) * ((n + c->bn - 1) / c->bn);
@@ -546,6 +786,7 @@ const char* dg_status_string(int status) {
     case DG_ERR_NO_DEVICE: return "no usable gfx950 device";
     case DG_ERR_HIP: return "HIP runtime error";
     case DG_ERR_INTERNAL: return "internal error";
+    case DG_ERR_WORKSPACE: return "split-K workspace must grow during graph capture";
     default: return "unknown status";
   }
 }
@@ -554,21 +795,7 @@ const char* dg_last_error_message(void) { return g_last_error.c_str(); }
 
 int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb, uint16_t* d,
                    int m, int n, int k, dg_stream_t stream) {
-  if (!a || !sfa || !b || !sfb || !d) return fail(DG_ERR_INVALID_ARGUMENT, "null pointer argument");
-  if (m < 0) return fail(DG_ERR_INVALID_ARGUMENT, "m must be >= 0 (got %d)", m);
-  if (int s = check_k_n(n, k)) return s;
-  if (int s = check_rows(m, k)) return s;
-  if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d))
-    return fail(DG_ERR_MISALIGNED, "pointers must be 16-byte aligned");
-  if (m == 0) return ok();
-  int dev;
-  DeviceInfo* info;
-  if (int s = current_device(&dev, &info)) return s;
-  const Config* c;
-  if (int s = dense_config(dg::kFp8, m, n, info, &c)) return s;
-  dg::GemmParams p{};
-  p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d;
-  return launch_dense(c, p, dev, info, m, n, k, k / 128, stream);
+  return fp8_gemm(a, sfa, b, sfb, d, m, n, k, stream);
 }
 
 int dg_bf16_gemm_nt(const uint16_t* a, const uint16_t* b, uint16_t* d, int m, int n, int k, dg_stream_t stream) {

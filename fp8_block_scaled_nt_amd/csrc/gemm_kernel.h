@@ -8,11 +8,12 @@
 // and masked layouts; unified block scheduler with rasterisation).  The
 // mechanism here is gfx950's own:
 //
-//  * one v_mfma_scale_f32_16x16x128_f8f6f4 per 16x16 fragment covers exactly
-//    one 128-wide K slab, so its fp32 result p is the slab's partial sum;
+//  * one v_mfma_f32_16x16x128_f8f6f4 per 16x16 fragment (the unscaled form
+//    of the f8f6f4 MFMA) covers exactly one 128-wide K slab, so its fp32
+//    result p is the slab's partial sum;
 //  * promotion: acc += p * (sa[row] * sb[col block]) in fp32 VGPRs after each
-//    slab (the MFMA's own E8M0 scales stay neutral: the fp32 block scales
-//    are not powers of two);
+//    slab (the block scales are arbitrary fp32 values, not the power-of-two
+//    E8M0 scales the MFMA's scaled form could apply);
 //  * operand tiles move HBM/L2 -> LDS with LDS DMA (buffer_load_dwordx4 ...
 //    lds, no VGPR staging), NST-stage buffered, one workgroup barrier per
 //    slab (the schedules below vary this);
@@ -547,6 +548,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
     sb_idx[j] = EPI == kEpiSwigluFp8 ? (j < FN / 2 ? 0 : 1) : ((n0 + wn * TN + j * 16) >> 7) - nb0;
   // a wave's columns lie in one block
   constexpr bool kSbUniform = EPI == kEpiBf16 && (128 % TN) == 0;
+  // Otherwise they lie in two (TN = 112 of a 224-wide tile, or the gate and up
+  // halves of a SwiGLU tile): fragments j < sb_split take the first block's
+  // scale, the others the second's.  The fp8 main loop below is compiled once
+  // per possible split (the choice is made once per tile), so the scale
+  // products are formed once per row fragment and block.
+  static_assert(TN <= 128, "a wave's columns span at most two B scale blocks");
+  int sb_split = FN;
+  #pragma unroll
+  for (int j = FN - 1; j > 0; --j)
+    if (sb_idx[j] != sb_idx[0]) sb_split = j;
+  sb_split = __builtin_amdgcn_readfirstlane(sb_split);
   // fragments of this wave that hold at least one valid row
   int fm_valid = FM;
   if (VAR == kMasked) {
@@ -718,6 +730,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
     for (int s0 = 0; s0 <= NST - 2; ++s0)
       if (s0 < KB) issue_slab(s0, s0);
 
+    // the main loop, compiled once per B scale split (kSplit: fragments of
+    // this wave in the first block; FN when all are in one)
+    auto main_loop = [&](auto split_c) {
+    constexpr int kSplit = decltype(split_c)::value;
     for (int kb = 0; kb < KB; ++kb) {
       // slab kb's DMA must have landed (in every wave: then the barrier); the
       // loads issued after it may stay in flight.
@@ -836,31 +852,42 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
         }
         continue;
       }
-      #pragma unroll
-      for (int t = 0; t < F + kLag; ++t) {
-        if (t < F) {
-          const int i = t / FN, j = t % FN;
-          if (VAR != kMasked || i < fm_valid) {
-            if (j == 0 && i + kPf < FM && (VAR != kMasked || i + kPf < fm_valid)) load_a(i + kPf);
-            pr[t % (kLag + 1)] = mfma_fp8_16x16x128(abuf[i % kAbuf], bf[j]);
+      {
+        const float sb_first = sbv[0], sb_second = sbv[FN - 1];
+        #pragma unroll
+        for (int t = 0; t < F + kLag; ++t) {
+          if (t < F) {
+            const int i = t / FN, j = t % FN;
+            if (VAR != kMasked || i < fm_valid) {
+              if (j == 0 && i + kPf < FM && (VAR != kMasked || i + kPf < fm_valid)) load_a(i + kPf);
+              pr[t % (kLag + 1)] = mfma_fp8_16x16x128(abuf[i % kAbuf], bf[j]);
+            }
           }
-        }
-        if (t >= kLag) {
-          const int u = t - kLag;
-          const int i = u / FN, j = u % FN;
-          if (VAR != kMasked || i < fm_valid) {
-            const v4f sc = sabuf[i % kSabuf] * sbv[j];
-            const v4f pv = pr[u % (kLag + 1)];
-            acc[i][j][0] = __builtin_fmaf(pv[0], sc[0], acc[i][j][0]);
-            acc[i][j][1] = __builtin_fmaf(pv[1], sc[1], acc[i][j][1]);
-            acc[i][j][2] = __builtin_fmaf(pv[2], sc[2], acc[i][j][2]);
-            acc[i][j][3] = __builtin_fmaf(pv[3], sc[3], acc[i][j][3]);
+          if (t >= kLag) {
+            const int u = t - kLag;
+            const int i = u / FN, j = u % FN;
+            if (VAR != kMasked || i < fm_valid) {
+              const v4f sc = sabuf[i % kSabuf] * (j < kSplit ? sb_first : sb_second);
+              const v4f pv = pr[u % (kLag + 1)];
+              acc[i][j][0] = __builtin_fmaf(pv[0], sc[0], acc[i][j][0]);
+              acc[i][j][1] = __builtin_fmaf(pv[1], sc[1], acc[i][j][1]);
+              acc[i][j][2] = __builtin_fmaf(pv[2], sc[2], acc[i][j][2]);
+              acc[i][j][3] = __builtin_fmaf(pv[3], sc[3], acc[i][j][3]);
+            }
           }
+          // keep this order: a promotion must not move up next to the MFMA
+          // that produces its input (that stalls the wave on the result)
+          __builtin_amdgcn_sched_barrier(0);
         }
-        // keep this order: a promotion must not move up next to the MFMA
-        // that produces its input (that stalls the wave on the result)
-        __builtin_amdgcn_sched_barrier(0);
       }
+    }
+    };
+    if constexpr (kSbUniform || DT != kFp8) {
+      main_loop(std::integral_constant<int, FN>{});
+    } else {
+      [&]<int... J>(std::integer_sequence<int, J...>) {
+        (void)((sb_split == J + 1 ? (main_loop(std::integral_constant<int, J + 1>{}), true) : false) || ...);
+      }(std::make_integer_sequence<int, FN>{});
     }
   }
 
@@ -969,10 +996,23 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   // ---- split-K fix-up: publish this split's partial tile; the last split
   // to arrive adds all partials in split order (deterministic) and goes on to
   // store D.  Partials are laid out fragment-native (each lane owns 16
-  // contiguous bytes per fragment) and move with SC1 buffer stores and loads,
-  // which are coherent across the per-XCD L2s (the agent-scope path), so no
-  // L2 write-back or invalidate is needed.  The reducer reads kChunk splits'
+  // contiguous bytes per fragment).  The reducer reads kChunk splits'
   // partials per batch; loads past the last split return zero.
+  //
+  // Why the hand-off is ordered across the per-XCD L2s without a release /
+  // acquire pair: the partial stores and the reducer's loads carry SC1, the
+  // agent-scope cache policy (the form of a relaxed agent-scope atomic store
+  // and load on this target), so a store completes only once it is written
+  // beyond the issuing XCD's L2 at the device coherence point, and a load is
+  // served from that point, not from a possibly stale L1 or L2 line.  Each
+  // thread waits vmcnt(0) for its own stores to complete; the barrier then
+  // puts every thread's completed stores before thread 0's agent-scope
+  // atomic, performed at the same point.  The reducer's atomic returns after
+  // every other split's atomic, hence after all their stores completed; its
+  // loads are issued only after that return is seen (a data dependency
+  // through the barrier), so they find the stored values.  A release/acquire
+  // atomic would add an L2 write-back and invalidate of every dirty line,
+  // which measured twice as slow as these coherent accesses on decode shapes.
   if constexpr (VAR == kDense && SCHED != kPingPong) if (p.splits > 1) {
     constexpr int kTileFloats = BM * BN;
     constexpr int kChunk = (FM * FN * 4) >= 128 ? 1 : 128 / (FM * FN * 4);

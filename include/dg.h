@@ -24,11 +24,24 @@
  *   keeps or allocates anything on behalf of a call's arguments.
  * - Every compute call is asynchronous on `stream` (0 = the null stream),
  *   performs no host<->device copy and no synchronisation, and reads no
- *   device value on the host.  The one device allocation is the split-K
- *   workspace of the dense calls (fp8, bf16, fp4), made or grown by the first
- *   call on a device that needs it; dg_reserve_workspace makes it ahead of
- *   time.  Apart from that first growth the calls are capturable into a HIP
- *   graph.
+ *   device value on the host; every one can be captured into a HIP graph
+ *   (see the workspace rule below).
+ * - Split-K workspace.  Dense calls (fp8, bf16, fp4) whose K is split over
+ *   several workgroups keep fp32 partial tiles and arrival counters in a
+ *   library-owned workspace, one per (device, stream).  Calls on one stream
+ *   share it in stream order; calls on different streams never share one, so
+ *   split-K calls may overlap in time on different streams.  A call that
+ *   needs more than its stream's workspace holds makes a larger one (one
+ *   hipMalloc, then a zero-fill kernel on `stream`; no device-wide
+ *   synchronisation); the smaller block is retired, not freed, and stays
+ *   allocated until the process ends, because a launch in flight or a graph
+ *   captured earlier may still use it.  While `stream` is capturing a graph
+ *   such a growth is refused with DG_ERR_WORKSPACE and nothing is enqueued:
+ *   size the workspace first with dg_reserve_workspace(bytes, stream), bytes
+ *   from dg_dense_workspace_size.  A captured call keeps using the workspace
+ *   its capture stream had; a replay must not overlap in time with other
+ *   split-K work on that same workspace (replaying on the capture stream, or
+ *   on any stream ordered with it, is safe).
  * - Layouts are packed and row-major:
  *     A       [m][k]               (masked: [num_groups][max_m][k])
  *     B       [n][k]               (grouped: [num_groups][n][k])
@@ -44,7 +57,9 @@
  *   dg_last_error_message() then describes the failure.
  * - D is overwritten (not accumulated) for valid rows only; every other
  *   element of D is left bit-for-bit untouched.
- * - No exception crosses this interface.  All functions are thread-safe.
+ * - No exception crosses this interface.  Every function may be called from
+ *   several host threads at once (the workspace table is locked; the last
+ *   error message is kept per thread).
  */
 #ifndef DG_H
 #define DG_H
@@ -65,7 +80,9 @@ typedef enum {
   DG_ERR_MISALIGNED = 3,        /* a pointer not 16-byte aligned                 */
   DG_ERR_NO_DEVICE = 4,         /* no usable gfx950 device                       */
   DG_ERR_HIP = 5,               /* a HIP runtime call or kernel launch failed     */
-  DG_ERR_INTERNAL = 6
+  DG_ERR_INTERNAL = 6,
+  DG_ERR_WORKSPACE = 7          /* the stream's split-K workspace would have to
+                                   grow while the stream is capturing a graph */
 } dg_status;
 
 /*
@@ -74,12 +91,11 @@ typedef enum {
  * and >= 1 respectively; a partial last 128-row block of B uses its own scale
  * row of sfb.  When the output tiles alone cannot fill the GPU (skinny m,
  * or few tiles, as in one GPU's shard of a larger GEMM), the K dimension is
- * split over several workgroups whose fp32 partial tiles meet in a
- * library-owned device workspace and are added in a fixed order, so results
- * stay bit-for-bit reproducible.  The workspace is allocated (or grown) by
- * the first call that needs it on a device; that call is then not
- * graph-capturable (dg_reserve_workspace with dg_dense_workspace_size avoids
- * this), and concurrent split-K calls on one device must not overlap in time.
+ * split over several workgroups whose fp32 partial tiles meet in the
+ * stream's split-K workspace (see the conventions above) and are added in a
+ * fixed order, so results stay bit-for-bit reproducible.  m <= 64 (decode
+ * shapes) takes a kernel that deals 128-wide K slabs of 64-row tiles to the
+ * workgroups in equal runs; larger m the tiled kernels.
  */
 int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
                    uint16_t* d, int m, int n, int k, dg_stream_t stream);
@@ -240,12 +256,15 @@ int dg_quantize_a_1x128_fp4(const float* x, uint8_t* q, float* sfa, int m, int k
 int dg_quantize_b_128x128_fp4(const float* x, uint8_t* q, float* sfb, int n, int k, dg_stream_t stream);
 
 /*
- * Pre-allocate the split-K workspace of the current device with room for
- * `bytes` of partial tiles (a tile of BM x BN outputs takes 4*BM*BN bytes per
- * split).  Calls that then fit allocate nothing.  Synchronises the device
- * when it has to grow the workspace.
+ * Size the split-K workspace of `stream` on the current device to hold at
+ * least `bytes` of partial tiles (dg_dense_workspace_size gives a call's
+ * need), so that later calls on that stream that fit allocate nothing and
+ * can be captured.  Growing allocates one block and enqueues a zero-fill
+ * kernel on `stream`; it does not synchronise the device.  Returns
+ * DG_ERR_WORKSPACE, with nothing done, if it would have to grow while
+ * `stream` is capturing.
  */
-int dg_reserve_workspace(size_t bytes);
+int dg_reserve_workspace(size_t bytes, dg_stream_t stream);
 
 /* Operand types of the dense entry points, for dg_dense_workspace_size. */
 typedef enum { DG_DTYPE_FP8 = 0, DG_DTYPE_BF16 = 1, DG_DTYPE_FP4 = 2 } dg_dtype;
@@ -253,9 +272,9 @@ typedef enum { DG_DTYPE_FP8 = 0, DG_DTYPE_BF16 = 1, DG_DTYPE_FP4 = 2 } dg_dtype;
 /*
  * Bytes of split-K workspace that a dense call of this dtype and shape
  * (dg_fp8_gemm_nt, dg_bf16_gemm_nt or dg_fp4_gemm_nt, m x n, K of k values)
- * makes on the current device: 0 when the call does not split K.  Passing
- * it to dg_reserve_workspace before capturing such calls in a graph keeps
- * them from allocating.  Same shape checks as the GEMM calls (k a positive
+ * needs on the current device: 0 when the call does not split K.  Passing
+ * it to dg_reserve_workspace for a stream before capturing such calls on
+ * that stream keeps them from allocating.  Same shape checks as the GEMM calls (k a positive
  * multiple of 128, 64 or 256 for fp8, bf16 and fp4, m >= 0, n >= 1), an
  * unknown dtype is DG_ERR_INVALID_ARGUMENT, and *bytes is 0 on any error.
  */

@@ -6,6 +6,8 @@ quantisers (CPU), results from the library (GPU), expected values from the
 oracle's GEMMs (CPU).
 """
 
+import ctypes
+
 import numpy as np
 import torch
 
@@ -30,6 +32,10 @@ def slab_major(sfa_logical):
 def slab_major_to_logical(sfa_dev, rows):
     """Inverse of slab_major for a downloaded buffer."""
     return np.ascontiguousarray(sfa_dev[:, :rows].T)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def codes_to_device(codes, dev):

@@ -159,3 +159,59 @@ def test_a_removed_guard_is_caught(device_asm):
                 return
             last_dma = line.rstrip().endswith(" lds")
     pytest.fail("no guard behind a DMA found")
+
+
+M0_WRITE = re.compile(r"^\s+s_\w+\s+m0,")
+
+
+def m0_writes_outside_guards(lines):
+    """Every instruction that writes M0 in a GEMM kernel, unless it sits in a
+    guard sequence: s_and_saveexec_b64 (EXEC cleared), the EXEC = 0 guard
+    load, the M0 write, the EXEC restore, then the LDS DMA.  Returns the
+    offending (kernel, instruction) pairs and the number of M0 writes seen."""
+    found, total, kernel = [], 0, None
+    code = []
+    for line in lines:
+        m = LABEL.match(line)
+        if m:
+            kernel = m.group(1)
+            continue
+        s = line.split(";")[0].rstrip()
+        if kernel and kernel.startswith("_ZN2dg18gemm_fp8_nt_kernel") and s.strip() and not s.startswith("."):
+            code.append((kernel, s))
+    for i, (kern, s) in enumerate(code):
+        if not M0_WRITE.match(s):
+            continue
+        total += 1
+        ok = (i >= 2 and i + 2 < len(code)
+              and code[i - 2][1].strip().startswith("s_and_saveexec_b64")
+              and GUARD.match(code[i - 1][1])
+              and code[i + 1][1].strip().startswith("s_mov_b64 exec,")
+              and code[i + 2][1].rstrip().endswith(" lds"))
+        if not ok:
+            found.append((kern, s.strip()))
+    return found, total
+
+
+def test_every_m0_write_is_inside_a_guard(device_asm):
+    # M0 is written only by the DMA asm, each write between its guard load and
+    # the EXEC restore that precedes the DMA: the compiler never writes M0 in
+    # these kernels (its own LDS DMA code writes the next M0 right after a DMA,
+    # the pattern the guard exists for)
+    found, total = m0_writes_outside_guards(device_asm)
+    assert total > 1000
+    assert not found, found[:10]
+
+
+def test_m0_check_flags_a_bare_write():
+    lines = ["_ZN2dg18gemm_fp8_nt_kernelILi64EEEvNS_10GemmParamsE:",
+             "\ts_and_saveexec_b64 s[10:11], 0",
+             "\tbuffer_load_dword v3, v3, s[4:7], 0 offen",
+             "\ts_mov_b32 m0, s12",
+             "\ts_mov_b64 exec, s[10:11]",
+             "\tbuffer_load_dwordx4 v3, s[4:7], s8 offen lds",
+             "\ts_mov_b32 m0, s13",
+             "\tbuffer_load_dwordx4 v4, s[4:7], s8 offen lds"]
+    found, total = m0_writes_outside_guards(lines)
+    assert total == 2
+    assert found == [("_ZN2dg18gemm_fp8_nt_kernelILi64EEEvNS_10GemmParamsE", "s_mov_b32 m0, s13")]

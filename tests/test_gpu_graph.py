@@ -27,6 +27,7 @@ def test_graph_replays_match_eager(gpu):
     sfa2 = torch.empty_like(sfa)
     d = torch.empty_like(d_eager)
     stream = torch.cuda.Stream()
+    dg.reserve_workspace(dg.dense_workspace_size(64, 2112, 7168), stream)  # the capture stream's workspace
     graph = torch.cuda.CUDAGraph()
     print("[case] graph capture of quantise A + GEMM (decode shape)", flush=True)
     with torch.cuda.stream(stream):
@@ -80,7 +81,8 @@ def test_graph_swiglu_and_fp4(gpu):
     qa4 = torch.empty((64, 512), dtype=torch.uint8, device=gpu)
     sfa4 = dg.empty_sfa(64, 1024, None, gpu)
     d4 = torch.empty((64, 300), dtype=torch.bfloat16, device=gpu)
-    dg.reserve_workspace(16 << 20)
+    stream = torch.cuda.Stream()
+    dg.reserve_workspace(16 << 20, stream)  # the capture stream's split-K workspace
 
     def run():
         dg.m_grouped_fp8_gemm_nt_masked_swiglu((qa, sfa), (qb, sfb), (hq, hs), mm)
@@ -95,7 +97,6 @@ def test_graph_swiglu_and_fp4(gpu):
         return [o.view(torch.uint8).cpu().numpy().copy() for o in (hq, hs, d4)]
 
     refs = eager_refs()
-    stream = torch.cuda.Stream()
     graph = torch.cuda.CUDAGraph()
     print("[case] graph capture of FC1 + SwiGLU and FP4 quantise + GEMM", flush=True)
     with torch.cuda.stream(stream):
@@ -121,10 +122,13 @@ def test_workspace_size_then_graph_of_mid_shape(gpu):
     assert dg.dense_workspace_size(4096, 7168, 16384) == 0                       # 448 big tiles, no split
     assert dg.dense_workspace_size(4096, 896, 16384) == 224 * 2 * 128 * 128 * 4  # 128 x 128 tiles, 2 splits
     assert dg.dense_workspace_size(0, 896, 16384) == 0
+    # m <= 16: the skinny kernel, 64 x 32 tiles with at most 5 contributors each
+    assert dg.dense_workspace_size(16, 2112, 7168) == 66 * 5 * tile
     m, n, k = 1024, 896, 2048  # 56 tiles of 128 x 128, 8 splits
     need = dg.dense_workspace_size(m, n, k)
     assert need == 56 * 8 * 128 * 128 * 4
-    dg.reserve_workspace(need)
+    stream = torch.cuda.Stream()
+    dg.reserve_workspace(need, stream)
     rng = np.random.default_rng(5)
     qa, sfa = dg.quantize_a_1x128(torch.from_numpy(rng.standard_normal((m, k), dtype=np.float32)).to(gpu))
     qb, sfb = dg.quantize_b_128x128(torch.from_numpy(rng.standard_normal((n, k), dtype=np.float32)).to(gpu))
@@ -133,7 +137,6 @@ def test_workspace_size_then_graph_of_mid_shape(gpu):
     torch.cuda.synchronize()
     ref = d_eager.view(torch.uint8).cpu().numpy()
     d = torch.empty_like(d_eager)
-    stream = torch.cuda.Stream()
     graph = torch.cuda.CUDAGraph()
     print("[case] graph capture of a split-K mid shape 1024x896x2048", flush=True)
     with torch.cuda.stream(stream):

@@ -24,7 +24,8 @@ pytestmark = pytest.mark.gpu
 DENSE_CONFIGS = ["dense_256x256_w8_s2", "dense_256x128_w8_s3", "dense_128x256_w8_s3", "dense_128x128_w4_s3",
                  "dense_128x128_w4_s2", "dense_64x64_w4_s3", "dense_64x64_w4_s8", "dense_64x32_w4_s4", "dense_256x224_w8_s2",
                  "dense_128x256_w4_s3_wide", "dense_256x256_w8_s2_pp", "dense_256x128_w4_s2",
-                 "dense_256x128_w4_s3", "dense_128x256_w4_s3", "dense_128x256_w4_s2_sb"]
+                 "dense_256x128_w4_s3", "dense_128x256_w4_s3", "dense_128x256_w4_s2_sb", "dense_128x224_w4_s2_sb",
+                 "dense_128x224_w4_s2"]
 
 
 def dense_case(m, n, k, seed, b_std=1.0):
@@ -69,7 +70,7 @@ def test_dense_small_workload_matches(gpu):
     qa, sa = oracle.quantize_a_1x128(x["a"])
     qb, sb = oracle.quantize_b_128x128(x["b"])
     d = check_dense(gpu, qa, sa, qb, sb, "dense_128x512x1024 seed 0")
-    # run-to-run determinism (no atomics in the GEMM)
+    # run-to-run determinism (split-K partials are added in a fixed order)
     d2, _ = H.run_dense(qa, sa, qb, sb, gpu)
     assert np.array_equal(H.d_bits(d), H.d_bits(d2))
 
@@ -383,3 +384,39 @@ def test_bf16_gemm_forced_split_k(gpu, monkeypatch):
     assert res["ok"], res
     d2, _ = H.run_bf16(a, b, gpu)
     assert np.array_equal(H.d_bits(d), H.d_bits(d2))
+
+
+@pytest.mark.parametrize("cfg,m,n,k", [
+    ("dense_256x256_w8_s2", 1024, 1024, 512),   # 16 tiles: the grid is a multiple of 8, the XCD remap is active
+    ("dense_128x256_w4_s2_sb", 1024, 1024, 512),
+    ("dense_256x256_w8_s2", 768, 2048, 384),    # 24 tiles
+    ("dense_256x224_w8_s2", 1024, 1792, 512),   # 32 tiles, every wave column split across two B scale blocks
+    ("dense_128x224_w4_s2_sb", 1024, 1792, 512),
+])
+def test_dense_default_tiles_with_xcd_remap(gpu, cfg, m, n, k, monkeypatch):
+    """The large-shape default tiles, element by element, at shapes whose
+    workgroup count is a multiple of the 8 XCDs, so that the XCD-aware block
+    remap and the grouped raster are not the identity."""
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    check_dense(gpu, *dense_case(m, n, k, seed=13), label=f"{cfg} {m}x{n}x{k}")
+
+
+def test_contiguous_default_tile_with_xcd_remap(gpu, monkeypatch):
+    """contig_128x256_w4_s2_sb (the 4-expert default) on 8 experts x 128 rows,
+    N 512: 16 workgroups, a multiple of the 8 XCDs; every element against the
+    oracle."""
+    monkeypatch.setenv("DG_FORCE_CONFIG", "contig_128x256_w4_s2_sb")
+    group_rows = [128] * 8
+    n, k = 512, 512
+    x = W.draw_contiguous(group_rows, n, k, seed=14)
+    qa, sa = oracle.quantize_a_1x128(x["a"])
+    qbs = [oracle.quantize_b_128x128(x["b"][g]) for g in range(len(group_rows))]
+    qb = np.stack([q for q, _ in qbs])
+    sb = np.stack([s for _, s in qbs])
+    print("[case] contig_128x256_w4_s2_sb 8x128 rows", flush=True)
+    d, flat = H.run_contiguous(qa, sa, qb, sb, x["m_indices"], gpu)
+    r, valid = oracle.grouped_contiguous_ref(qa, sa, qb, sb, x["m_indices"])
+    assert valid.all()
+    res = oracle.tolerance_check(H.d_float(d), r)
+    assert res["ok"], res
+    assert H.guard_untouched(flat, d.numel())

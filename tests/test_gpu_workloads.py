@@ -6,7 +6,14 @@ The oracle cannot compute the full outputs in seconds, so it computes sampled
 entries one by one: it quantises (on the CPU, from the same fp32 draws) the
 A rows and B 128-row blocks those entries need, checks that the GPU's codes
 and scales for them are bit-identical, and evaluates each sampled entry in
-fp64.  The tolerance's rms term uses the sample's rms.  For the masked
+fp64.  The tolerance's rms term uses the sample's rms (the rms of the whole
+output is not available without the whole output; over a sample of a few
+hundred entries drawn from every tile row and column it is within a few
+percent of it, and the term only matters for entries near zero).  The two
+dense shapes the oracle finishes in seconds (128 x 512 x 1024 and the
+64 x 2112 x 7168 decode shape) are compared in full instead.  Every output
+element is checked on the device to have been written (no 0xFFFF sentinel
+left) for the dense, contiguous and K-grouped workloads; for the masked
 workload every row past masked_m is checked to hold the sentinel; for all of
 them the guard band after D must be untouched.
 """
@@ -57,7 +64,9 @@ def check_sampled(label, d_sel, qa_rows, sa_rows, b_codes, b_scales, rows_ix, co
     return res
 
 
-def dense_case(gpu, name):
+def dense_case(gpu, name, whole=False):
+    """Full-size dense workload; with whole=True every output element is
+    compared with the oracle (shapes the oracle finishes in seconds)."""
     w = W.WORKLOADS[name]
     m, n, k = w.shape["m"], w.shape["n"], w.shape["k"]
     x = W.draw(name)
@@ -68,6 +77,16 @@ def dense_case(gpu, name):
     dg.fp8_gemm_nt((qa, sfa), (qb, sfb), d)
     torch.cuda.synchronize()
     assert H.guard_untouched(flat, d.numel())
+    # every element was written (results are finite, the 0xFFFF sentinel is a NaN)
+    assert not bool((d.view(torch.int16) == -1).any())
+    if whole:
+        qa_r, sa_r = oracle.quantize_a_1x128(x["a"])
+        qb_r, sb_r = oracle.quantize_b_128x128(x["b"])
+        assert np.array_equal(qa.view(torch.uint8).cpu().numpy(), qa_r)
+        assert np.array_equal(qb.view(torch.uint8).cpu().numpy(), qb_r)
+        res = oracle.tolerance_check(H.d_float(d), oracle.gemm_nt_ref(qa_r, sa_r, qb_r, sb_r))
+        assert res["ok"], (name, res)
+        return res
     rng = np.random.default_rng(99)
     rows = np.unique(np.concatenate([[0, m - 1], pick(rng, m, 12)]))
     bsel, cols = plan_cols(rng, n, 3, 24)
@@ -91,11 +110,11 @@ def dense_case(gpu, name):
 
 
 def test_dense_small_full(gpu):
-    dense_case(gpu, "dense_128x512x1024")
+    dense_case(gpu, "dense_128x512x1024", whole=True)
 
 
 def test_dense_decode_full(gpu):
-    dense_case(gpu, "dense_decode_64x2112x7168")
+    dense_case(gpu, "dense_decode_64x2112x7168", whole=True)
 
 
 def test_dense_large_full(gpu):
@@ -124,6 +143,7 @@ def test_contiguous_full(gpu):
     dg.m_grouped_fp8_gemm_nt_contiguous((qa, sfa), (qb, sfb), d, torch.from_numpy(idx).to(gpu))
     torch.cuda.synchronize()
     assert H.guard_untouched(flat, d.numel())
+    assert not bool((d.view(torch.int16) == -1).any())  # no padding rows: every element written
     rng = np.random.default_rng(98)
     sfb_dev = sfb.cpu().numpy()
     for e in range(g):
