@@ -28,7 +28,7 @@ _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("DG_LIBRARY") or os.path.join(_PKG_DIR, "libdg.so")
 
 __all__ = [
-    "DGError", "lib", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous",
+    "DGError", "lib", "fp8_gemm_nt", "fp8_gemm_nt_noalloc", "m_grouped_fp8_gemm_nt_contiguous",
     "m_grouped_fp8_gemm_nt_masked", "m_grouped_fp8_gemm_nt_masked_swiglu", "quantize_a_1x128", "quantize_b_128x128",
     "k_grouped_fp8_gemm_nt", "bf16_gemm_nt", "fp4_gemm_nt", "quantize_a_1x128_fp4", "quantize_b_128x128_fp4", "get_m_alignment_for_contiguous_layout", "get_sfa_ld", "empty_sfa",
     "profile_next_launch",
@@ -48,6 +48,7 @@ _lib = None
 _vp, _ci = ctypes.c_void_p, ctypes.c_int
 _SIGNATURES = {
     "dg_fp8_gemm_nt": [_vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _vp],
+    "dg_fp8_gemm_nt_noalloc": [_vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _vp],
     "dg_m_grouped_fp8_gemm_nt_contiguous": [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _vp],
     "dg_m_grouped_fp8_gemm_nt_masked": [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _vp],
     "dg_m_grouped_fp8_gemm_nt_masked_swiglu": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _vp],
@@ -180,6 +181,27 @@ def fp8_gemm_nt(a_pair, b_pair, d):
     if tuple(sfb.shape) != ((n + 127) // 128, k // 128):
         raise ValueError("sfb must be [ceil(n/128), k/128]")
     _check(lib().dg_fp8_gemm_nt(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(d), m, n, k, _stream()))
+    return d
+
+
+def fp8_gemm_nt_noalloc(a_pair, b_pair, d):
+    """fp8_gemm_nt for callers that cannot allocate device memory: split-K
+    scratch comes from the library's static per-GPU array (calls that
+    overlap in time on one GPU race)."""
+    a, sfa = a_pair
+    b, sfb = b_pair
+    _need(a, "a", _FP8, 2)
+    _need(b, "b", _FP8, 2)
+    _need(d, "d", (torch.bfloat16,), 2)
+    _need(sfa, "sfa", (torch.float32,), 2)
+    _need(sfb, "sfb", (torch.float32,), 2)
+    m, k = a.shape
+    n = b.shape[0]
+    if b.shape[1] != k or tuple(d.shape) != (m, n):
+        raise ValueError(f"shape mismatch a{tuple(a.shape)} b{tuple(b.shape)} d{tuple(d.shape)}")
+    if tuple(sfa.shape) != (k // 128, get_sfa_ld(m)) or tuple(sfb.shape) != ((n + 127) // 128, k // 128):
+        raise ValueError("scale shape mismatch")
+    _check(lib().dg_fp8_gemm_nt_noalloc(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(d), m, n, k, _stream()))
     return d
 
 

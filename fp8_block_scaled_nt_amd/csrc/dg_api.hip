@@ -355,18 +355,67 @@ int ensure_workspace(int dev, hipStream_t stream, size_t partial_bytes, char** b
   return DG_OK;
 }
 
-// Where a split-K call's counters and partial tiles live: the calling
-// stream's workspace block.
+// ---- allocation-free split-K scratch (dg_fp8_gemm_nt_noalloc): one static
+// device array, held by every GPU the library runs on until the process
+// ends.  Host code never passes the array's name to a kernel (in host code it
+// names a host-side stand-in); it uses the device address that
+// hipGetSymbolAddress returns, taken once per device with that device current.
+constexpr size_t kScratchCounterInts = (size_t)1 << 14;       // arrival counters: tiles per call
+constexpr size_t kScratchPartialBytes = (size_t)16 << 20;     // partial tiles
+constexpr size_t kScratchHeader = kScratchCounterInts * sizeof(int);
+constexpr size_t kScratchBytes = kScratchHeader + kScratchPartialBytes;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+char* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+int scratch_address(int dev, char** ptr) {
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (g_scratch_err[dev] != hipSuccess) (void)hipGetLastError();
+    g_scratch_ptr[dev] = (char*)p;
+  });
+  if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev])
+    return fail(DG_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(g_scratch_err[dev]));
+  *ptr = g_scratch_ptr[dev];
+  return DG_OK;
+}
+
+// Where a split-K call takes its workspace: the calling stream's block, grown
+// on demand (fixed == nullptr), or the static scratch of the allocation-free
+// entry point (fixed = its device address), whose counters are cleared for
+// every call by a fill kernel on the call's stream (a kernel, not a memset,
+// so that a captured call records a kernel node).
+struct WsSource {
+  char* fixed = nullptr;
+};
+
 struct WsView {
   int* counters = nullptr;
   char* partial = nullptr;
 };
 
-int get_workspace(int dev, hipStream_t stream, size_t partial_bytes, WsView* v) {
-  char* base = nullptr;
-  if (int s = ensure_workspace(dev, stream, partial_bytes, &base)) return s;
-  v->counters = (int*)base;
-  v->partial = base + kWsHeader;
+int get_workspace(const WsSource& src, int dev, hipStream_t stream, size_t partial_bytes, long long counters_used,
+                  WsView* v) {
+  if (!src.fixed) {
+    char* base = nullptr;
+    if (int s = ensure_workspace(dev, stream, partial_bytes, &base)) return s;
+    v->counters = (int*)base;
+    v->partial = base + kWsHeader;
+    return DG_OK;
+  }
+  if (partial_bytes > kScratchPartialBytes || counters_used > (long long)kScratchCounterInts)
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "this call needs %zu bytes of split-K scratch and %lld counters; the static "
+                "scratch holds %zu bytes and %zu counters", partial_bytes, counters_used, kScratchPartialBytes,
+                kScratchCounterInts);
+  v->counters = (int*)src.fixed;
+  v->partial = src.fixed + kScratchHeader;
+  hipLaunchKernelGGL(zero_ints_kernel, dim3((unsigned)((counters_used + 255) / 256)), dim3(256), 0, stream,
+                     v->counters, counters_used);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DG_ERR_HIP, "scratch counter clear failed: %s", hipGetErrorString(e));
   return DG_OK;
 }
 
@@ -513,7 +562,7 @@ int dense_config(int dtype, int m, int n, const DeviceInfo* info, const Config**
 // points; k_bytes is K in bytes (one per fp8 value, two per bf16 value, half
 // per fp4 value) and scale_slabs the number of 128-wide scale slabs of K.
 int launch_dense(const Config* c, dg::GemmParams& p, int dev, const DeviceInfo* info, int m, int n, int k_bytes,
-                 int scale_slabs, dg_stream_t stream) {
+                 int scale_slabs, dg_stream_t stream, const WsSource& ws = WsSource{}) {
   if (int s = ensure_kernel_attributes()) return s;
   p.num_groups = 1;
   fill_common(p, *c, m, n, k_bytes);
@@ -529,7 +578,7 @@ int launch_dense(const Config* c, dg::GemmParams& p, int dev, const DeviceInfo* 
       return fail(DG_ERR_UNSUPPORTED_SHAPE, "split-K grid too large (%d x %d)", p.num_tiles, p.splits);
     const size_t part = (size_t)p.num_tiles * p.splits * c->bm * c->bn * sizeof(float);
     WsView v;
-    if (int s = get_workspace(dev, (hipStream_t)stream, part, &v)) return s;
+    if (int s = get_workspace(ws, dev, (hipStream_t)stream, part, p.num_tiles, &v)) return s;
     p.ws_partial = (float*)v.partial;
     p.ws_count = v.counters;
   }
@@ -602,7 +651,7 @@ int skinny_config(int m, int n, int kb, const DeviceInfo* info, SkinnyPlan* plan
 }
 
 int launch_skinny(const SkinnyPlan& pl, const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
-                  uint16_t* d, int m, int n, int k, int dev, dg_stream_t stream) {
+                  uint16_t* d, int m, int n, int k, int dev, dg_stream_t stream, const WsSource& ws = WsSource{}) {
   if (int s = ensure_kernel_attributes()) return s;
   dg::SkinnyParams p{};
   p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d;
@@ -615,7 +664,7 @@ int launch_skinny(const SkinnyPlan& pl, const uint8_t* a, const float* sfa, cons
   p.max_contrib = pl.max_contrib;
   if (pl.ws_bytes > 0) {
     WsView v;
-    if (int s = get_workspace(dev, (hipStream_t)stream, pl.ws_bytes, &v)) return s;
+    if (int s = get_workspace(ws, dev, (hipStream_t)stream, pl.ws_bytes, pl.tiles_n, &v)) return s;
     p.ws_partial = (float*)v.partial;
     p.ws_count = v.counters;
   }
@@ -677,9 +726,10 @@ int quantize_b(const void* kernel, const float* x, uint8_t* q, float* sfb, int n
 }
 
 
-// The dense fp8 call.
+// The dense fp8 call, with the split-K workspace of the calling stream or,
+// for the allocation-free entry point, the static scratch.
 int fp8_gemm(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb, uint16_t* d, int m, int n, int k,
-             dg_stream_t stream) {
+             dg_stream_t stream, bool use_scratch) {
   if (!a || !sfa || !b || !sfb || !d) return fail(DG_ERR_INVALID_ARGUMENT, "null pointer argument");
   if (m < 0) return fail(DG_ERR_INVALID_ARGUMENT, "m must be >= 0 (got %d)", m);
   if (int s = check_k_n(n, k)) return s;
@@ -690,14 +740,17 @@ int fp8_gemm(const uint8_t* a, const float* sfa, const uint8_t* b, const float* 
   int dev;
   DeviceInfo* info;
   if (int s = current_device(&dev, &info)) return s;
+  WsSource ws;
+  if (use_scratch)
+    if (int s = scratch_address(dev, &ws.fixed)) return s;
   SkinnyPlan sp;
   if (int s = skinny_config(m, n, k / 128, info, &sp)) return s;
-  if (sp.c) return launch_skinny(sp, a, sfa, b, sfb, d, m, n, k, dev, stream);
+  if (sp.c) return launch_skinny(sp, a, sfa, b, sfb, d, m, n, k, dev, stream, ws);
   const Config* c;
   if (int s = dense_config(dg::kFp8, m, n, info, &c)) return s;
   dg::GemmParams p{};
   p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d;
-  return launch_dense(c, p, dev, info, m, n, k, k / 128, stream);
+  return launch_dense(c, p, dev, info, m, n, k, k / 128, stream, ws);
 }
 
 }  // namespace
@@ -795,7 +848,12 @@ const char* dg_last_error_message(void) { return g_last_error.c_str(); }
 
 int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb, uint16_t* d,
                    int m, int n, int k, dg_stream_t stream) {
-  return fp8_gemm(a, sfa, b, sfb, d, m, n, k, stream);
+  return fp8_gemm(a, sfa, b, sfb, d, m, n, k, stream, false);
+}
+
+int dg_fp8_gemm_nt_noalloc(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb, uint16_t* d,
+                           int m, int n, int k, dg_stream_t stream) {
+  return fp8_gemm(a, sfa, b, sfb, d, m, n, k, stream, true);
 }
 
 int dg_bf16_gemm_nt(const uint16_t* a, const uint16_t* b, uint16_t* d, int m, int n, int k, dg_stream_t stream) {

@@ -41,7 +41,8 @@
  *   from dg_dense_workspace_size.  A captured call keeps using the workspace
  *   its capture stream had; a replay must not overlap in time with other
  *   split-K work on that same workspace (replaying on the capture stream, or
- *   on any stream ordered with it, is safe).
+ *   on any stream ordered with it, is safe).  dg_fp8_gemm_nt_noalloc uses a
+ *   static per-GPU array instead and allocates nothing.
  * - Layouts are packed and row-major:
  *     A       [m][k]               (masked: [num_groups][max_m][k])
  *     B       [n][k]               (grouped: [num_groups][n][k])
@@ -99,6 +100,25 @@ typedef enum {
  */
 int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
                    uint16_t* d, int m, int n, int k, dg_stream_t stream);
+
+/*
+ * dg_fp8_gemm_nt for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, kernels and results as dg_fp8_gemm_nt (bit for bit), but
+ * a split-K call takes its fp32 partial tiles and arrival counters from a
+ * static array of the library, one per GPU (16 MiB of partials and 16384
+ * counters, held until the process ends), instead of the stream's workspace;
+ * the call never allocates, frees or synchronises.  Each call clears the
+ * counters it uses with a small kernel on `stream` before the GEMM.  A call
+ * that would need more scratch than the array holds returns
+ * DG_ERR_UNSUPPORTED_SHAPE with nothing enqueued (the 64 x 2112 x 7168
+ * decode shape takes 2.6 MiB).  All calls on one GPU share the array, so
+ * calls of this entry point that overlap in time on one GPU (two streams, or
+ * two threads) race and give wrong results; dg_fp8_gemm_nt has no such
+ * limit.
+ */
+int dg_fp8_gemm_nt_noalloc(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                           uint16_t* d, int m, int n, int k, dg_stream_t stream);
 
 /*
  * MoE grouped GEMM, contiguous layout ("DeepSeek open-source week day 3",
