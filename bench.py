@@ -54,12 +54,14 @@ def parse():
                     help="'all', 'main', or a comma list of workload names for the extra figures")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--mode", choices=["bench", "counters", "oracle"], default="bench",
+    ap.add_argument("--mode", choices=["bench", "counters", "oracle", "tiles"], default="bench",
                     help="counters: run plain kernels of known traffic (1 GiB fill, 1 GiB read; "
                          "calibration for rocprofv3 FETCH_SIZE/WRITE_SIZE), then eager GEMM launches "
                          "of the headline workload and of the --workloads list ('main' = none), "
                          "print nothing; oracle: time the CPU oracle's GEMM on the five configurations "
-                         "and print one JSON line")
+                         "and print one JSON line; tiles: the large dense GEMM's 256 x 256 tile, "
+                         "unsplit, at 256, 448 and 512 tiles (N 4096, 7168, 8192), --kernel-launches "
+                         "back-to-back launches each, one JSON line")
     return ap.parse_args()
 
 
@@ -402,6 +404,46 @@ ORACLE_CONFIGS = ["dense_128x512x1024", "dense_decode_64x2112x7168", "dense_larg
                   "moe_contiguous_4x8192_n4096_k7168", "moe_masked_16x256_n4096_k7168"]
 
 
+def tile_count_timing(np, W, launches):
+    """The large dense GEMM (M 4096, K 16384) with its 256 x 256 tile and no
+    split at N = 4096, 7168 and 8192: 256 tiles (one per CU), 448 and 512.
+    Back-to-back launches timed by wall clock between two synchronisations,
+    so the cost of the last, partial wave of tiles shows against the work."""
+    import torch
+
+    import fp8_block_scaled_nt_amd as dg
+    dev = torch.device("cuda:0")
+    os.environ["DG_FORCE_CONFIG"] = "dense_256x256_w8_s2"
+    os.environ["DG_SPLIT_K"] = "1"
+    m, k = 4096, 16384
+    rows = []
+    try:
+        for n in (4096, 7168, 8192):
+            x = W.draw_dense(m, n, k, seed=0)
+            qa, sfa = dg.quantize_a_1x128(torch.from_numpy(x["a"]).to(dev))
+            qb, sfb = dg.quantize_b_128x128(torch.from_numpy(x["b"]).to(dev))
+            del x
+            d = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            for _ in range(3):
+                dg.fp8_gemm_nt((qa, sfa), (qb, sfb), d)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(launches):
+                dg.fp8_gemm_nt((qa, sfa), (qb, sfb), d)
+            torch.cuda.synchronize()
+            us = (time.perf_counter() - t0) / launches * 1e6
+            tiles = (m // 256) * (n // 256)
+            rows.append({"n": n, "tiles": tiles, "us": round(us, 1),
+                         "tflops": round(2.0 * m * n * k / us / 1e6, 1)})
+            print(f"[tiles] N {n}: {tiles} tiles, {us:.1f} us", file=sys.stderr, flush=True)
+            del qa, sfa, qb, sfb, d
+            torch.cuda.empty_cache()
+    finally:
+        os.environ.pop("DG_FORCE_CONFIG", None)
+        os.environ.pop("DG_SPLIT_K", None)
+    return rows
+
+
 def oracle_timing(np, W):
     """The oracle's GEMM on each of the five configurations, on the host's
     cores: the two large ones once, the others best of three.  Inputs are the
@@ -460,6 +502,9 @@ def main():
     import workloads as W
     if args.mode == "oracle":
         print(json.dumps({"oracle_cpu_timing": oracle_timing(np, W)}))
+        return 0
+    if args.mode == "tiles":
+        print(json.dumps({"tile_count_timing": tile_count_timing(np, W, args.kernel_launches)}))
         return 0
 
     import torch

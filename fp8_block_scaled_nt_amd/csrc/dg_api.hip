@@ -111,8 +111,6 @@ const Config* configs(int* count) {
       make_config<256, 256, 2, 4, 2, dg::kDense, dg::kPingPong>("dense_256x256_w8_s2_pp"),
       make_config<128, 256, 1, 4, 2, dg::kDense, dg::kSingleB>("dense_128x256_w4_s2_sb"),
       make_config<256, 224, 4, 2, 2, dg::kDense>("dense_256x224_w8_s2"),
-      make_config<128, 224, 2, 2, 2, dg::kDense, dg::kSingleB>("dense_128x224_w4_s2_sb"),
-      make_config<128, 224, 2, 2, 2, dg::kDense>("dense_128x224_w4_s2"),
       make_config<128, 256, 1, 4, 3, dg::kDense>("dense_128x256_w4_s3_wide"),
       make_config<256, 128, 4, 2, 3, dg::kDense>("dense_256x128_w8_s3"),
       make_config<256, 128, 2, 2, 2, dg::kDense>("dense_256x128_w4_s2"),
@@ -629,11 +627,15 @@ bool skinny_plan(const SkinnyConfig* c, int m, int n, int kb, const DeviceInfo* 
 // The skinny configuration a dense fp8 call uses (nullptr: the tiled kernels):
 // DG_FORCE_CONFIG when it names a skinny configuration (then m must be at
 // most 64), else skinny_64x32_w16_stagea for m <= 16 while one run of units
-// per CU covers the shape.  Measured on N 2112, K 7168 (kernel time with
-// events, median): m 1, 8, 16: 10.1-10.4 against 11.1-11.3 us for the
-// tiled split-K kernel; m 32: level (11.0); m 48 and 64: 11.6 and 12.1
-// against 11.0 and 10.8 us, where reloading A in every run costs more than
-// the tiled kernel's pipelined LDS staging.
+// per CU covers the shape and each run keeps at least 12 of its 16 waves
+// busy.  Measured (kernel time with events, median, m 1-16): N 2112 K 7168
+// 9.4-9.6 against 10.9-11.2 us for the tiled split-K kernel, N 7168 K 2048
+// 8.7-8.9 against 9.8-9.9 us (14 units per run); with fewer units per run
+// the partial-tile hand-off dominates: N 576 K 7168 (4 per run) 11.0
+// against 8.7 us, N 512 K 1024 (1 per run) 8.4 against 5.3 us.  At m 32
+// it is level, at m 48 and 64 behind (11.6 and 12.1 against 11.0 and
+// 10.8 us on N 2112), where reloading A in every run costs more than the
+// tiled kernel's pipelined LDS staging.
 int skinny_config(int m, int n, int kb, const DeviceInfo* info, SkinnyPlan* plan) {
   plan->c = nullptr;
   const char* e = getenv("DG_FORCE_CONFIG");
@@ -645,7 +647,8 @@ int skinny_config(int m, int n, int kb, const DeviceInfo* info, SkinnyPlan* plan
     return DG_OK;
   }
   SkinnyPlan pl;
-  if (m <= 16 && skinny_plan(find_skinny("skinny_64x32_w16_stagea"), m, n, kb, info, &pl) && pl.grid <= info->cus)
+  if (m <= 16 && skinny_plan(find_skinny("skinny_64x32_w16_stagea"), m, n, kb, info, &pl) && pl.grid <= info->cus &&
+      pl.per >= 12)
     *plan = pl;
   return DG_OK;
 }

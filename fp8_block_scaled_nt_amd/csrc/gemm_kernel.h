@@ -283,6 +283,38 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return (bid % kNumXcd) * (nblocks / kNumXcd) + bid / kNumXcd;
 }
 
+// Tile number v of workgroup b when only the first `total` workgroups have
+// a tile: consecutive numbers go to one XCD (workgroup b runs on XCD b % 8)
+// and every XCD gets total / 8 of them, the first total % 8 XCDs one more.
+// A bijection of [0, total) for any total.
+__device__ __forceinline__ int xcd_deal(int b, int total) {
+  const int x = b % kNumXcd;
+  const int q = total / kNumXcd, r = total % kNumXcd;
+  return x * q + (x < r ? x : r) + b / kNumXcd;
+}
+
+// Masked layout: the count of expert e clamped to [0, max_m]; 0 past the
+// last expert.
+__device__ __forceinline__ int masked_count(const GemmParams& p, int e) {
+  if (e >= p.num_groups) return 0;
+  const int c = p.masked_m[e];
+  return c < 0 ? 0 : (c > p.m ? p.m : c);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave, in DPP moves (no LDS):
+// shifts by 1, 2, 4 and 8 lanes inside each row of 16, then row 0's total
+// into row 1 and row 2's into row 3 (row_bcast:15), then lane 31's total
+// into rows 2 and 3 (row_bcast:31).  Lanes without a source add 0.
+__device__ __forceinline__ int wave_prefix_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
 // Number of slab DMA batches a wave has issued after the one of slab kb, at
 // the top of iteration kb: the prologue issues slabs 0..NST-2 and iteration
 // i issues slab i+NST-1 (nothing for slabs >= KB).
@@ -339,13 +371,47 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
 
   // ---- tile -> (group, tile_m, tile_n[, split])
   int g = 0, tm, tn, tile_id = 0, split = 0;
+  int masked_rows = 0;  // masked: the expert's count, clamped to [0, max_m]
   if (VAR == kMasked) {
-    // an expert's tiles are consecutive, and the XCD remap keeps consecutive
-    // tiles on one XCD: the expert's A rows are fetched into one L2 only
-    const int t = xcd_remap(blockIdx.x, gridDim.x);
-    const int per_g = p.tiles_m * p.tiles_n;
-    g = t / per_g;
-    const int r = t - g * per_g;
+    // Only tiles with valid rows are visited.  The grid covers every
+    // (expert, tile) of the max_m slab, so it does not depend on the counts
+    // (a captured graph stays valid as they change); the valid tiles, tiles_n
+    // per started BM-row block of each count, are numbered expert-major and
+    // the first `total` workgroups take one each, dealt so that an expert's
+    // consecutive tiles share one XCD's L2 and the 8 XCDs get equal shares.
+    // The other workgroups exit having read the counts.  Every wave derives
+    // the same values from the counts (lane e of a pass reads expert e).
+    // Experts are read 64 at a time (lane e of a pass holds expert base + e);
+    // with at most 64 experts one pass does both the count and the search.
+    const auto tiles_of = [&](int c) { return (c + BM - 1) / BM * p.tiles_n; };
+    int c = masked_count(p, lane);
+    int x = tiles_of(c);
+    int incl = wave_prefix_sum(x);
+    int total = __builtin_amdgcn_readlane(incl, 63);
+    for (int base = 64; base < p.num_groups; base += 64)
+      total += __builtin_amdgcn_readlane(wave_prefix_sum(tiles_of(masked_count(p, base + lane))), 63);
+    if ((int)blockIdx.x >= total) return;
+    const int v = xcd_deal(blockIdx.x, total);
+    int before = 0;  // valid tiles of the experts before g
+    g = -1;
+    for (int base = 0; base < p.num_groups; base += 64) {
+      if (base > 0) {
+        c = masked_count(p, base + lane);
+        x = tiles_of(c);
+        incl = wave_prefix_sum(x);
+      }
+      const unsigned long long hit = __ballot(before + incl > v);
+      if (hit) {
+        const int l = __ffsll(hit) - 1;
+        g = base + l;
+        before += __builtin_amdgcn_readlane(incl - x, l);
+        masked_rows = __builtin_amdgcn_readlane(c, l);
+        break;
+      }
+      before += __builtin_amdgcn_readlane(incl, 63);
+    }
+    if (g < 0 || g >= p.num_groups) return;  // not reached: v < total
+    const int r = v - before;
     tm = r / p.tiles_n;
     tn = r - tm * p.tiles_n;
   } else if (VAR == kKGrouped) {
@@ -398,10 +464,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
     B += (size_t)expert * p.n * p.k;
     SFB += (size_t)expert * p.nb_count * p.sk_count;
   } else if (VAR == kMasked) {
-    int cnt = p.masked_m[g];
-    cnt = cnt < 0 ? 0 : (cnt > p.m ? p.m : cnt);
-    if (m0 >= cnt) return;  // masked early exit: nothing valid in this tile
-    valid_rows = cnt;
+    if (m0 >= masked_rows) return;  // not reached: the tile walk above visits valid tiles only
+    valid_rows = masked_rows;
     A += (size_t)g * p.m * p.k;
     SFA += (size_t)g * p.sk_count * p.sfa_ld;
     B += (size_t)g * p.n * p.k;

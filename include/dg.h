@@ -94,9 +94,11 @@ typedef enum {
  * or few tiles, as in one GPU's shard of a larger GEMM), the K dimension is
  * split over several workgroups whose fp32 partial tiles meet in the
  * stream's split-K workspace (see the conventions above) and are added in a
- * fixed order, so results stay bit-for-bit reproducible.  m <= 64 (decode
- * shapes) takes a kernel that deals 128-wide K slabs of 64-row tiles to the
- * workgroups in equal runs; larger m the tiled kernels.
+ * fixed order, so results stay bit-for-bit reproducible.  For m <= 16, on
+ * shapes whose 128-wide K slabs of 64-row tiles fill one run of at least 12
+ * slabs per CU, a kernel that deals those slabs to the workgroups in equal
+ * runs is used instead; every other shape takes the tiled kernels.  The
+ * choice never changes a result beyond the split-K summation order.
  */
 int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
                    uint16_t* d, int m, int n, int k, dg_stream_t stream);

@@ -24,8 +24,7 @@ pytestmark = pytest.mark.gpu
 DENSE_CONFIGS = ["dense_256x256_w8_s2", "dense_256x128_w8_s3", "dense_128x256_w8_s3", "dense_128x128_w4_s3",
                  "dense_128x128_w4_s2", "dense_64x64_w4_s3", "dense_64x64_w4_s8", "dense_64x32_w4_s4", "dense_256x224_w8_s2",
                  "dense_128x256_w4_s3_wide", "dense_256x256_w8_s2_pp", "dense_256x128_w4_s2",
-                 "dense_256x128_w4_s3", "dense_128x256_w4_s3", "dense_128x256_w4_s2_sb", "dense_128x224_w4_s2_sb",
-                 "dense_128x224_w4_s2"]
+                 "dense_256x128_w4_s3", "dense_128x256_w4_s3", "dense_128x256_w4_s2_sb"]
 
 
 def dense_case(m, n, k, seed, b_std=1.0):
@@ -163,6 +162,37 @@ def test_masked(gpu, cfg, max_m, monkeypatch):
     assert res["ok"], res
     bits = H.d_bits(d)
     assert np.all(bits[~valid] == H.SENTINEL)
+    assert H.guard_untouched(flat, d.numel())
+
+
+@pytest.mark.parametrize("cfg", [None, "masked_64x64_w4_s3", "masked_256x256_w8_s2_pp", "masked_128x256_w8_s3"])
+def test_masked_many_experts(gpu, cfg, monkeypatch):
+    """150 experts, more than two 64-expert chunks of the valid-tile walk:
+    empty experts, experts past max_m and runs of empty experts across the
+    chunk boundaries; the valid tiles are far fewer than the grid."""
+    if cfg:
+        monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    g, max_m, n, k = 150, 80, 144, 256
+    rng = np.random.default_rng(31)
+    masked_m = rng.integers(0, max_m + 1, g).astype(np.int32)
+    masked_m[rng.integers(0, g, 40)] = 0
+    masked_m[60:70] = 0
+    masked_m[127:131] = 0
+    masked_m[63], masked_m[64], masked_m[128] = max_m + 7, 1, 65
+    masked_m[-1] = max_m
+    x = W.draw_masked(g, max_m, n, k, seed=32, masked_m=masked_m)
+    qas = [oracle.quantize_a_1x128(x["a"][i]) for i in range(g)]
+    qa = np.stack([q for q, _ in qas])
+    sa = np.stack([s for _, s in qas])
+    qbs = [oracle.quantize_b_128x128(x["b"][i]) for i in range(g)]
+    qb = np.stack([q for q, _ in qbs])
+    sb = np.stack([s for _, s in qbs])
+    print(f"[case] masked many experts {cfg}", flush=True)
+    d, flat = H.run_masked(qa, sa, qb, sb, masked_m, gpu)
+    r, valid = oracle.grouped_masked_ref(qa, sa, qb, sb, masked_m)
+    res = oracle.tolerance_check(H.d_float(d), r, valid[:, :, None])
+    assert res["ok"], res
+    assert np.all(H.d_bits(d)[~valid] == H.SENTINEL)
     assert H.guard_untouched(flat, d.numel())
 
 
@@ -391,7 +421,6 @@ def test_bf16_gemm_forced_split_k(gpu, monkeypatch):
     ("dense_128x256_w4_s2_sb", 1024, 1024, 512),
     ("dense_256x256_w8_s2", 768, 2048, 384),    # 24 tiles
     ("dense_256x224_w8_s2", 1024, 1792, 512),   # 32 tiles, every wave column split across two B scale blocks
-    ("dense_128x224_w4_s2_sb", 1024, 1792, 512),
 ])
 def test_dense_default_tiles_with_xcd_remap(gpu, cfg, m, n, k, monkeypatch):
     """The large-shape default tiles, element by element, at shapes whose
