@@ -46,6 +46,36 @@ def test_random_dense(gpu, m, n, kslabs):
     assert H.guard_untouched(flat, d.numel())
 
 
+def small_m_shapes(count):
+    """Decode-like shapes: m 1..16 and N x K with 3100-4000 units of a 64x32
+    tile and a 128-wide slab, the range where the skinny kernel is the default."""
+    rng = np.random.default_rng(RNG_SEED + 16)
+    out = []
+    for _ in range(count):
+        m = int(rng.integers(1, 17))
+        n = int(rng.integers(1000, 4200))
+        tiles = (n + 31) // 32
+        lo, hi = -(-3100 // tiles), 4000 // tiles
+        out.append((m, n, int(rng.integers(lo, hi + 1))))
+    return out
+
+
+@pytest.mark.parametrize("m,n,kslabs", small_m_shapes(6))
+@pytest.mark.parametrize("cfg", [None, "skinny_64x32_w16_stagea", "dense_64x32_w4_s4"])
+def test_random_small_m(gpu, m, n, kslabs, cfg, monkeypatch):
+    if cfg:
+        monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    k = 128 * kslabs
+    x = W.draw_dense(m, n, k, seed=m * 11 + n)
+    qa, sa = oracle.quantize_a_1x128(x["a"])
+    qb, sb = oracle.quantize_b_128x128(x["b"])
+    print(f"[case] random small m {m}x{n}x{k} {cfg}", flush=True)
+    d, flat = H.run_dense(qa, sa, qb, sb, gpu)
+    res = oracle.tolerance_check(H.d_float(d), oracle.gemm_nt_ref(qa, sa, qb, sb))
+    assert res["ok"], res
+    assert H.guard_untouched(flat, d.numel())
+
+
 @pytest.mark.parametrize("m,n,kslabs", shapes("fp4", 8))
 def test_random_fp4(gpu, m, n, kslabs):
     k = 256 * ((kslabs + 1) // 2)
