@@ -183,14 +183,23 @@ def kernel_time_us(torch, dg, launch, rot, n_launch, warm=20):
         e.record()  # materialise the underlying HIP events
     torch.cuda.synchronize()
     with CLOCK:
+        t0 = time.perf_counter()
         for i in range(n_launch):
             dg.profile_next_launch(starts[i], stops[i])
             launch(rot[warm + i])
         torch.cuda.synchronize()
+        window_ms = (time.perf_counter() - t0) * 1e3
     times = sorted(starts[i].elapsed_time(stops[i]) * 1e3 for i in range(n_launch))
     pct = lambda q: times[min(len(times) - 1, int(q * len(times)))]
+    sclk = CLOCK.summary()
+    if sclk is not None:
+        # amdsmi reports the clock level the power manager has set; between
+        # short launches that is an idle level, so the window and the share
+        # of it the kernels kept the GPU busy go with the samples
+        sclk["window_ms"] = round(window_ms, 2)
+        sclk["busy_share"] = round(sum(times) / 1e3 / window_ms, 3)
     return {"avg": sum(times) / len(times), "median": pct(0.5), "p10": pct(0.1), "p90": pct(0.9),
-            "sclk": CLOCK.summary()}
+            "sclk": sclk}
 
 
 def setup_workload(torch, np, dg, W, name, dev):

@@ -478,9 +478,10 @@ int check_rows(long long rows, int k) {
   return DG_OK;
 }
 
-// The 256 x 256 tile (one workgroup per CU) while its tiles alone keep more
-// than half the CUs busy, so that it needs no split-K; below that, 128 x 128
-// tiles (two per CU, split over K when still too few) finish sooner.  The
+// Large tiles (256 x 256 for BF16 and FP4, 128 x 256 two per CU for FP8)
+// while 256 x 256 tiles alone would keep more than half the CUs busy, so
+// that no split-K is needed; below that, 128 x 128 tiles (two per CU, split
+// over K when still too few) finish sooner.  The
 // N- and M-shards of the large GEMM over 8 GPUs, 4096 x 896 x 16384 and
 // 512 x 7168 x 16384, run in 83-90 us against 107 us for 256 x 256 tiles
 // split 4 ways; 2048 x 7168 x 16384 (224 big tiles) keeps 256 x 256 tiles,
@@ -539,7 +540,11 @@ const Config* dense_default_config(int dtype, int m, int n, const DeviceInfo* in
       return find_config(mid ? "fp4_128x128_w4_s2" : "fp4_256x256_w8_s2", dg::kDense, dg::kFp4);
     default: {
       if (m <= 64) return find_config(n <= 4096 ? "dense_64x32_w4_s4" : "dense_64x64_w4_s3", dg::kDense);
-      if (!mid) return find_config("dense_256x256_w8_s2", dg::kDense);
+      // large: the 128 x 256 one-B-buffer tile, two workgroups per CU.  Medians
+      // of five alternating runs against 256 x 256: 4096 x 7168 x 16384 467
+      // against 489 us, 2048 x 7168 x 16384 248 against 260, 4096 x 4096 x
+      // 16384 264 against 266, 4096 x 8192 x 16384 522 against 516.
+      if (!mid) return find_config("dense_128x256_w4_s2_sb", dg::kDense);
       if (few) return find_config(n <= 1024 ? "dense_64x32_w4_s4" : "dense_64x64_w4_s3", dg::kDense);
       if (t128 <= 72 && n >= 1024) return find_config("dense_128x128_w4_s3", dg::kDense);
       return find_config("dense_128x128_w4_s2", dg::kDense);

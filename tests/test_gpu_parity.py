@@ -420,6 +420,8 @@ def test_bf16_gemm_forced_split_k(gpu, monkeypatch):
     ("dense_256x256_w8_s2", 1024, 1024, 512),   # 16 tiles: the grid is a multiple of 8, the XCD remap is active
     ("dense_128x256_w4_s2_sb", 1024, 1024, 512),
     ("dense_256x256_w8_s2", 768, 2048, 384),    # 24 tiles
+    ("dense_128x256_w4_s2_sb", 768, 2048, 384),  # 48 tiles
+    ("dense_128x256_w4_s2_sb", 1000, 2000, 640),  # ragged rows and columns, 64 tiles
     ("dense_256x224_w8_s2", 1024, 1792, 512),   # 32 tiles, every wave column split across two B scale blocks
 ])
 def test_dense_default_tiles_with_xcd_remap(gpu, cfg, m, n, k, monkeypatch):
