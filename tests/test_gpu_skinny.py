@@ -1,4 +1,5 @@
-"""GPU parity of the skinny-M dense path (m <= 64, the decode shapes) and the
+"""GPU parity of the skinny-M dense kernel (any m <= 64 when a skinny
+configuration is forced; the default for m <= 16 where it is faster) and the
 split-K workspace rules: per-stream workspaces, overlapping calls on two
 streams, graph replays after the workspace has grown, and the status a
 capture gets when the workspace would have to grow.
@@ -85,14 +86,13 @@ def _device_operands(case, gpu):
             H.codes_to_device(qb, gpu), H.f32_to_device(sb, gpu))
 
 
-@pytest.mark.parametrize("cfg", [None, "dense_64x32_w4_s4"])
+@pytest.mark.parametrize("cfg", ["skinny_64x32_w16_stagea", "dense_64x32_w4_s4"])
 def test_two_streams_overlap(gpu, cfg, monkeypatch):
     """Two split-K calls of the decode shape enqueued on two streams with no
     synchronisation between them (each stream has its own workspace): both
     outputs match the oracle element by element, for the skinny kernel and
     for the tiled split-K kernel."""
-    if cfg:
-        monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
     cases = [dense_case(64, 2112, 7168, seed=s, b_std=0.02) for s in (11, 12)]
     refs = [oracle.gemm_nt_ref(*c) for c in cases]
     ops = [_device_operands(c, gpu) for c in cases]

@@ -43,11 +43,22 @@ def run(entry, c, gpu):
     return status, d, flat
 
 
+SKINNY_TILE_BYTES = 64 * 32 * 4  # one fp32 partial tile of the skinny kernel
+
+
 @pytest.mark.parametrize("shapes", [
-    [(64, 2112, 7168, 0.02), (17, 520, 1280, 1.0)],   # skinny split-K, then a smaller skinny call
-    [(128, 512, 1024, 1.0), (96, 200, 512, 1.0)],     # tiled split-K (64 x 32 tiles), then smaller
-])
+    # the skinny split-K kernel (m <= 16, 14 and 12 K-slab units per run), then a smaller call
+    [(8, 2112, 7168, 0.02), (5, 1800, 7168, 1.0)],
+    # the tiled split-K kernel on the decode shape, then a smaller tiled call
+    [(64, 2112, 7168, 0.02), (17, 520, 1280, 1.0)],
+    # tiled split-K with 64 x 32 tiles on a small dense shape, then smaller
+    [(128, 512, 1024, 1.0), (96, 200, 512, 1.0)],
+], ids=["skinny", "tiled-decode", "tiled-small"])
 def test_noalloc_matches_default_entry_point(gpu, shapes):
+    if shapes[0][0] <= 16:
+        # the skinny plans: 66 and 57 tiles of 64 x 32, 5 and 6 partial slots each
+        assert dg.dense_workspace_size(8, 2112, 7168) == 66 * 5 * SKINNY_TILE_BYTES
+        assert dg.dense_workspace_size(5, 1800, 7168) == 57 * 6 * SKINNY_TILE_BYTES
     for i, (m, n, k, b_std) in enumerate(shapes):
         c = case(m, n, k, seed=40 + i, b_std=b_std)
         print(f"[case] noalloc {m}x{n}x{k}", flush=True)
