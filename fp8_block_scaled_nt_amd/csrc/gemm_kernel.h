@@ -25,7 +25,9 @@
 //    16 distinct 16-byte bank groups, so ds_read_b128 is conflict-free;
 //  * the blockIdx -> tile map is XCD-aware: the 8 XCDs each take a
 //    contiguous run of a grouped-raster tile order, so tiles that share A
-//    rows or B columns sit in the same L2.
+//    rows or B columns sit in the same L2.  On the masked layout only
+//    the tiles with valid rows are numbered, and the first workgroups take
+//    them, dealt evenly over the XCDs.
 //
 // MFMA operand layout (probed on gfx950): lane l of a 16x16x128 fp8 operand
 // holds 32 K-bytes of row (l % 16); any K order works as long as A and B use
