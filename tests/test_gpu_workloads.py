@@ -117,6 +117,12 @@ def test_dense_decode_full(gpu):
     dense_case(gpu, "dense_decode_64x2112x7168", whole=True)
 
 
+def test_dense_decode_small_batch_full(gpu):
+    # m = 8: the skinny split-K kernel's default shape
+    assert dg.dense_workspace_size(8, 2112, 7168) == 66 * 5 * 64 * 32 * 4
+    dense_case(gpu, "dense_decode_8x2112x7168", whole=True)
+
+
 def test_dense_large_full(gpu):
     dense_case(gpu, "dense_large_4096x7168x16384")
 
