@@ -114,7 +114,7 @@ int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const f
  * counters it uses with a small kernel on `stream` before the GEMM.  A call
  * that would need more scratch than the array holds returns
  * DG_ERR_UNSUPPORTED_SHAPE with nothing enqueued (the 64 x 2112 x 7168
- * decode shape takes 2.6 MiB).  All calls on one GPU share the array, so
+ * decode shape takes 3.6 MiB).  All calls on one GPU share the array, so
  * calls of this entry point that overlap in time on one GPU (two streams, or
  * two threads) race and give wrong results; dg_fp8_gemm_nt has no such
  * limit.
