@@ -32,8 +32,9 @@
  *   share it in stream order; calls on different streams never share one, so
  *   split-K calls may overlap in time on different streams.  A call that
  *   needs more than its stream's workspace holds makes a larger one (one
- *   hipMalloc, then a zero-fill kernel on `stream`; no device-wide
- *   synchronisation); the smaller block is retired, not freed, and stays
+ *   hipMalloc, then a zero-fill kernel on `stream`; the library frees
+ *   nothing, so it adds no hipFree synchronisation); the smaller block is
+ *   retired, not freed, and stays
  *   allocated until the process ends, because a launch in flight or a graph
  *   captured earlier may still use it.  While `stream` is capturing a graph
  *   such a growth is refused with DG_ERR_WORKSPACE and nothing is enqueued:
