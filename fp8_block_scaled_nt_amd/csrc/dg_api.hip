@@ -961,14 +961,18 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, cons
 //    CU): 166-202 us for c = 160-256.
 //  * the 256 x 256 interleaved schedule leads up to c = 160 (123 against
 //    128 us), the ping-pong one from c = 192 (131-139 against 140-164 us).
+//  * a later sweep on the same inputs (counts uniform on 0..c, medians): for
+//    c = 128 the 128-row tile takes 104 us against 123 us interleaved and
+//    127 us ping-pong; for c = 192 ping-pong 139-141, interleaved 145-148,
+//    the 128-row tile 184 us.
 // So: max_m <= 128 (no expert can pass 128 rows) or a typical count
-// (expected_m) up to 48 picks the 128-row tile when there are enough of its
+// (expected_m) up to 64 picks the 128-row tile when there are enough of its
 // tiles to cover half the CUs; a typical count up to 80 the interleaved
 // 256 x 256 schedule; larger or unknown (0) counts the ping-pong one.
 enum class MaskedTile { kRows128, kInterleaved, kPingPong };
 MaskedTile masked_tile(int num_groups, int max_m, int n, int expected_m, const DeviceInfo* info) {
   const bool enough = 2LL * num_groups * ((n + 255) / 256) >= info->cus;
-  if (enough && (max_m <= 128 || (expected_m > 0 && expected_m <= 48))) return MaskedTile::kRows128;
+  if (enough && (max_m <= 128 || (expected_m > 0 && expected_m <= 64))) return MaskedTile::kRows128;
   if (expected_m > 0 && expected_m <= 80) return MaskedTile::kInterleaved;
   return MaskedTile::kPingPong;
 }

@@ -174,7 +174,7 @@ def test_contiguous_full(gpu):
                                         ("moe_masked_16x256_c64_n4096_k7168", 518)])
 def test_masked_full(gpu, name, total):
     # the typical count passed as expected_m picks the ping-pong schedule for
-    # the first workload (mean 129) and the interleaved one for the second (32)
+    # the first workload (mean 129) and the 128-row tile for the second (32)
     w = W.WORKLOADS[name]
     g, max_m, n, k = w.shape["g"], w.shape["max_m"], w.shape["n"], w.shape["k"]
     x = W.draw(name)
