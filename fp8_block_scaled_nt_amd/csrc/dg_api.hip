@@ -522,7 +522,8 @@ int dense_splits(const Config* c, int num_tiles, int kb_count, const DeviceInfo*
 
 // The default configuration of a dense call (the rules and their
 // measurements are next to big_tiles_enough and in the config table).
-const Config* dense_default_config(int dtype, int m, int n, const DeviceInfo* info) {
+// kb: K in 128-byte slabs (k / 128 for fp8, 2 k / 128 for bf16, k / 256 for fp4).
+const Config* dense_default_config(int dtype, int m, int n, int kb, const DeviceInfo* info) {
   const bool mid = m <= 256 || n <= 256 || !big_tiles_enough(m, n, info);
   // Few 128 x 128 tiles: smaller tiles (four or more workgroups per CU), or
   // a third stage, keep more loads in flight per CU than split-K of the
@@ -539,14 +540,35 @@ const Config* dense_default_config(int dtype, int m, int n, const DeviceInfo* in
       if (few || (mid && t128 <= 72 && n >= 1024)) return find_config("fp4_64x64_w4_s3", dg::kDense, dg::kFp4);
       return find_config(mid ? "fp4_128x128_w4_s2" : "fp4_256x256_w8_s2", dg::kDense, dg::kFp4);
     default: {
-      if (m <= 64) return find_config(n <= 4096 ? "dense_64x32_w4_s4" : "dense_64x64_w4_s3", dg::kDense);
+      // m <= 64: 64 x 32 tiles up to N 4096, and up to N 8192 while K is
+      // short (at most 16 slabs): 64 x 7168 x 2048 in 10.0 against 11.3 us
+      // for 64 x 64, which leads at long K (64 x 7168 x 16384: 34.0 against
+      // 41.0 us) and at N 24576 (13.0 against 13.5 us).
+      if (m <= 64)
+        return find_config(n <= 4096 || (kb <= 16 && n <= 8192) ? "dense_64x32_w4_s4" : "dense_64x64_w4_s3",
+                           dg::kDense);
       // large: the 128 x 256 one-B-buffer tile, two workgroups per CU.  Medians
       // of five alternating runs against 256 x 256: 4096 x 7168 x 16384 467
       // against 489 us, 2048 x 7168 x 16384 248 against 260, 4096 x 4096 x
       // 16384 264 against 266, 4096 x 8192 x 16384 522 against 516.
       if (!mid) return find_config("dense_128x256_w4_s2_sb", dg::kDense);
-      if (few) return find_config(n <= 1024 ? "dense_64x32_w4_s4" : "dense_64x64_w4_s3", dg::kDense);
+      // few tiles; at m <= 128 with short K also up to 128 of them (128 x
+      // 12288 x 1536: 64 x 64 in 11.5 against 15.4 us for 128 x 128 with
+      // three stages and 20.7 us with two).  64 x 32 tiles where N is small,
+      // or at m <= 128 with up to 64 tiles and K up to 16 slabs: 128 x 7168 x
+      // 1536 in 10.0 against 11.4 us, 128 x 2112 x 1536 in 9.8 against 11.1,
+      // 128 x 7168 x 2048 in 11.3 against 11.7; with more tiles 64 x 64 leads
+      // (128 x 16384 x 1024: 10.0 against 12.3 us), and at long K too (128 x
+      // 2112 x 7168: 13.8 against 15.5 us).
+      if (few || (m <= 128 && t128 <= 128 && kb <= 12)) {
+        const bool narrow = n <= 1024 || (m <= 128 && t128 <= 64 && kb <= 16);
+        return find_config(narrow ? "dense_64x32_w4_s4" : "dense_64x64_w4_s3", dg::kDense);
+      }
       if (t128 <= 72 && n >= 1024) return find_config("dense_128x128_w4_s3", dg::kDense);
+      // short K (at most 12 slabs) where the two-per-CU tile would be split
+      // over K: three stages unsplit instead.  128 x 24576 x 1536 in 16.7
+      // against 22.7 us, 128 x 32768 x 512 in 9.2 against 19.2 us.
+      if (kb <= 12 && t128 <= info->cus) return find_config("dense_128x128_w4_s3", dg::kDense);
       return find_config("dense_128x128_w4_s2", dg::kDense);
     }
   }
@@ -554,9 +576,9 @@ const Config* dense_default_config(int dtype, int m, int n, const DeviceInfo* in
 
 // The configuration a dense call uses: DG_FORCE_CONFIG when it names one of
 // this dtype's dense configurations, else the default.
-int dense_config(int dtype, int m, int n, const DeviceInfo* info, const Config** out) {
+int dense_config(int dtype, int m, int n, int kb, const DeviceInfo* info, const Config** out) {
   if (int s = forced_config(dg::kDense, out, dtype)) return s;
-  if (!*out) *out = dense_default_config(dtype, m, n, info);
+  if (!*out) *out = dense_default_config(dtype, m, n, kb, info);
   if (!*out) return fail(DG_ERR_INTERNAL, "no dense configuration for dtype %d", dtype);
   return DG_OK;
 }
@@ -755,7 +777,7 @@ int fp8_gemm(const uint8_t* a, const float* sfa, const uint8_t* b, const float* 
   if (int s = skinny_config(m, n, k / 128, info, &sp)) return s;
   if (sp.c) return launch_skinny(sp, a, sfa, b, sfb, d, m, n, k, dev, stream, ws);
   const Config* c;
-  if (int s = dense_config(dg::kFp8, m, n, info, &c)) return s;
+  if (int s = dense_config(dg::kFp8, m, n, k / 128, info, &c)) return s;
   dg::GemmParams p{};
   p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d;
   return launch_dense(c, p, dev, info, m, n, k, k / 128, stream, ws);
@@ -823,7 +845,7 @@ int dg_dense_workspace_size(int dtype, int m, int n, int k, size_t* bytes) {
     }
   }
   const Config* c;
-  if (int s = dense_config(dtype, m, n, info, &c)) return s;
+  if (int s = dense_config(dtype, m, n, k_bytes / 128, info, &c)) return s;
   const long long tiles = (long long)((m + c->bm - 1) / c->bm) * ((n + c->bn - 1) / c->bn);
   if (tiles > (1LL << 27)) return fail(DG_ERR_UNSUPPORTED_SHAPE, "too many output tiles (%lld)", tiles);
   int per = 0;
@@ -878,7 +900,7 @@ int dg_bf16_gemm_nt(const uint16_t* a, const uint16_t* b, uint16_t* d, int m, in
   DeviceInfo* info;
   if (int s = current_device(&dev, &info)) return s;
   const Config* c;
-  if (int s = dense_config(dg::kBf16, m, n, info, &c)) return s;
+  if (int s = dense_config(dg::kBf16, m, n, 2 * k / 128, info, &c)) return s;
   dg::GemmParams p{};
   p.a = reinterpret_cast<const uint8_t*>(a);
   p.b = reinterpret_cast<const uint8_t*>(b);
@@ -902,7 +924,7 @@ int dg_fp4_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const f
   DeviceInfo* info;
   if (int s = current_device(&dev, &info)) return s;
   const Config* c;
-  if (int s = dense_config(dg::kFp4, m, n, info, &c)) return s;
+  if (int s = dense_config(dg::kFp4, m, n, k / 256, info, &c)) return s;
   dg::GemmParams p{};
   p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d;
   return launch_dense(c, p, dev, info, m, n, k / 2, k / 128, stream);
