@@ -532,12 +532,38 @@ const Config* dense_default_config(int dtype, int m, int n, int kb, const Device
   const bool few = mid && m <= 256 && t128 <= 64;
   switch (dtype) {
     case dg::kBf16:
-      if (m <= 64 || (few && n <= 1024)) return find_config("bf16_64x32_w4_s4", dg::kDense, dg::kBf16);
-      if (few && n <= 4096) return find_config("bf16_64x64_w4_s3", dg::kDense, dg::kBf16);
+      // kb counts 64-value slabs here.  From a sweep of the pages' shapes
+      // (medians, us): m <= 64 keeps 64 x 32 up to N 4096 and at N 7168 with
+      // K 2048 (12.5 against 13.5), 64 x 64 beyond (64 x 7168 x 16384: 58.9
+      // against 70.2; 64 x 32768 x 512: 9.3 against 10.9); m <= 128 with K up
+      // to 2048 takes 64 x 64 (128 x 32768 x 512: 13.6 against 20.4 for
+      // 128 x 128; 128 x 24576 x 1536: 28.5 against 32.7; 128 x 7168 x 2048:
+      // 16.7 against 24.4).
+      if (m <= 64) {
+        const bool narrow = n <= 4096 || (n <= 8192 && kb <= 32);
+        return find_config(narrow ? "bf16_64x32_w4_s4" : "bf16_64x64_w4_s3", dg::kDense, dg::kBf16);
+      }
+      if (few && n <= 1024) return find_config("bf16_64x32_w4_s4", dg::kDense, dg::kBf16);
+      if ((few && n <= 4096) || (m <= 128 && kb <= 32)) return find_config("bf16_64x64_w4_s3", dg::kDense, dg::kBf16);
       return find_config(mid ? "bf16_128x128_w4_s2" : "bf16_256x256_w8_s2", dg::kDense, dg::kBf16);
     case dg::kFp4:
-      if (m <= 64 || (few && n <= 1024)) return find_config("fp4_64x32_w4_s4", dg::kDense, dg::kFp4);
-      if (few || (mid && t128 <= 72 && n >= 1024)) return find_config("fp4_64x64_w4_s3", dg::kDense, dg::kFp4);
+      // kb counts 256-value slabs here.  From the same sweep: m <= 64 keeps
+      // 64 x 32 at N 2112 and at N up to 8192 with K up to 2048, 64 x 64
+      // elsewhere (64 x 7168 x 16384: 20.9 against 24.9; 64 x 24576 x 1536:
+      // 9.5 against 10.4).  m <= 128 with up to 64 tiles takes 64 x 32 at N up
+      // to 4096 with K up to 7168 and at N up to 8192 with K up to 2048
+      // (128 x 7168 x 2048: 9.4 against 10.6 for 64 x 64; 128 x 2112 x 7168:
+      // 11.9 against 12.7); longer K keeps 64 x 64 (128 x 7168 x 16384: 32.8
+      // against 41.4).  With K up to 2048 over more tiles 64 x 64 wins
+      // (128 x 24576 x 1536: 10.9 against 17.8 for 128 x 128).
+      if (m <= 64) {
+        const bool narrow = n <= 2112 || (n <= 8192 && kb <= 8);
+        return find_config(narrow ? "fp4_64x32_w4_s4" : "fp4_64x64_w4_s3", dg::kDense, dg::kFp4);
+      }
+      if ((few && n <= 1024) || (m <= 128 && t128 <= 64 && (n <= 4096 ? kb <= 28 : n <= 8192 && kb <= 8)))
+        return find_config("fp4_64x32_w4_s4", dg::kDense, dg::kFp4);
+      if (few || (mid && t128 <= 72 && n >= 1024) || (m <= 128 && kb <= 8))
+        return find_config("fp4_64x64_w4_s3", dg::kDense, dg::kFp4);
       return find_config(mid ? "fp4_128x128_w4_s2" : "fp4_256x256_w8_s2", dg::kDense, dg::kFp4);
     default: {
       // m <= 64: 64 x 32 tiles up to N 4096, and up to N 8192 while K is
