@@ -143,6 +143,7 @@ const Config* configs(int* count) {
       // K-grouped
       make_config<256, 256, 2, 4, 2, dg::kKGrouped>("kgrouped_256x256_w8_s2"),
       make_config<128, 128, 2, 2, 2, dg::kKGrouped>("kgrouped_128x128_w4_s2"),
+      make_config<128, 256, 1, 4, 2, dg::kKGrouped, dg::kSingleB>("kgrouped_128x256_w4_s2_sb"),
       // BF16 dense (find_config matches the dtype too, so DG_FORCE_CONFIG
       // names pick among these only for the bf16 entry point)
       make_config<256, 256, 2, 4, 2, dg::kDense, dg::kInterleaved, dg::kBf16>("bf16_256x256_w8_s2"),
@@ -1079,7 +1080,15 @@ int dg_k_grouped_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* 
   if (int s = current_device(&dev, &info)) return s;
   const Config* c;
   if (int s = forced_config(dg::kKGrouped, &c)) return s;
-  if (!c) c = find_config(m <= 256 || n <= 256 ? "kgrouped_128x128_w4_s2" : "kgrouped_256x256_w8_s2", dg::kKGrouped);
+  // M up to 2048: the one-B-buffer tile, 507 against 550 us for the 256 x 256
+  // tile on 4 x 8192 K, M 2048, N 7168.  At M 4096 the two are level (981
+  // against 983 us) and the one-B-buffer tile fetches twice the bytes from
+  // beyond L2 (4.0 against 2.0 GB per launch), so 256 x 256 stays.
+  if (!c)
+    c = find_config(m <= 256 || n <= 256 ? "kgrouped_128x128_w4_s2"
+                    : m <= 2048          ? "kgrouped_128x256_w4_s2_sb"
+                                         : "kgrouped_256x256_w8_s2",
+                    dg::kKGrouped);
   dg::GemmParams p{};
   p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.k_sizes = k_sizes;
   p.num_groups = num_groups;

@@ -336,7 +336,7 @@ def test_split_k_back_to_back_shapes(gpu, cfg, monkeypatch):
         check_dense(gpu, *dense_case(m, n, k, seed=11), label=f"back-to-back splits={splits}")
 
 
-@pytest.mark.parametrize("cfg", [None, "kgrouped_256x256_w8_s2", "kgrouped_128x128_w4_s2"])
+@pytest.mark.parametrize("cfg", [None, "kgrouped_256x256_w8_s2", "kgrouped_128x128_w4_s2", "kgrouped_128x256_w4_s2_sb"])
 @pytest.mark.parametrize("m,n,sizes,k_total", [
     (300, 520, [256, 0, 640, 128], 1280),   # ragged tiles, an empty group, two unused slabs
     (64, 2112, [1024, 512], 1536),           # skinny M, N with a 64-row partial scale block
