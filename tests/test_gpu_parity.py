@@ -341,6 +341,7 @@ def test_split_k_back_to_back_shapes(gpu, cfg, monkeypatch):
     (300, 520, [256, 0, 640, 128], 1280),   # ragged tiles, an empty group, two unused slabs
     (64, 2112, [1024, 512], 1536),           # skinny M, N with a 64-row partial scale block
     (520, 300, [128], 128),                  # one group, one slab
+    (512, 1024, [384, 640], 1024),           # 32 workgroups of 128 x 256 tiles: the XCD remap is active
 ])
 def test_k_grouped(gpu, cfg, m, n, sizes, k_total, monkeypatch):
     if cfg:
