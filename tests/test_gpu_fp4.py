@@ -84,7 +84,11 @@ def check_fp4(gpu, pa, sa, pb, sb, label):
 
 @pytest.mark.parametrize("m,n,k", [(128, 512, 1024), (1, 16, 256), (17, 40, 256), (200, 176, 512),
                                    (64, 2112, 512), (300, 520, 768), (513, 257, 256), (200, 2112, 1024),
-                                   (384, 2112, 512)])
+                                   (384, 2112, 512),
+                                   # each branch of the small-M tile rules: 64 x 32 at moderate N and
+                                   # short K, 64 x 64 for wide N, long K or many tiles of short K
+                                   (64, 3000, 2048), (64, 9000, 512), (64, 4200, 4096), (128, 5000, 2048),
+                                   (100, 3000, 4096), (128, 17000, 512)])
 def test_fp4_default_selection(gpu, m, n, k):
     check_fp4(gpu, *fp4_case(m, n, k, seed=m + n + k), label=f"fp4 {m}x{n}x{k}")
 

@@ -403,6 +403,21 @@ def test_bf16_gemm(gpu, cfg, m, n, k, monkeypatch):
     assert H.guard_untouched(flat, d.numel())
 
 
+@pytest.mark.parametrize("m,n,k", [(64, 4200, 512), (64, 9000, 256), (64, 5000, 3072), (100, 5000, 1024),
+                                   (128, 7168, 2048)])
+def test_bf16_default_tile_regions(gpu, m, n, k):
+    """Each branch of the BF16 small-M tile rules at its default choice:
+    64 x 32 up to N 8192 with short K, 64 x 64 for wider N, longer K, or
+    M up to 128 with K up to 2048."""
+    x = W.draw_dense(m, n, k, seed=m + 3 * n + k)
+    a, b = bf16_bits(x["a"]), bf16_bits(x["b"])
+    print(f"[case] bf16 default {m}x{n}x{k}", flush=True)
+    d, flat = H.run_bf16(a, b, gpu)
+    res = oracle.tolerance_check(H.d_float(d), oracle.bf16_gemm_nt_ref(a, b))
+    assert res["ok"], res
+    assert H.guard_untouched(flat, d.numel())
+
+
 def test_bf16_gemm_forced_split_k(gpu, monkeypatch):
     monkeypatch.setenv("DG_FORCE_CONFIG", "bf16_64x32_w4_s4")
     monkeypatch.setenv("DG_SPLIT_K", "5")
