@@ -52,6 +52,18 @@ def check_dense(gpu, qa, sa, qb, sb, label):
     (64, 2112, 512),
     (300, 520, 640),
     (513, 257, 256),
+    # each branch of the tile rules below the large shapes: 64 x 32 for M <= 64
+    # up to N 8192 with short K, 64 x 64 for wider N or longer K; M <= 128 with
+    # short K: 64 x 32 up to 64 tiles of 128 x 128, 64 x 64 up to 128; 51-72
+    # tiles: 128 x 128 with 3 stages; short K over at most one tile per CU: the
+    # same tile unsplit
+    (64, 7000, 2048),
+    (64, 5000, 3072),
+    (48, 9000, 512),
+    (128, 7168, 1536),
+    (128, 12000, 1536),
+    (384, 2112, 1024),
+    (384, 8192, 1024),
 ])
 def test_dense_default_selection(gpu, m, n, k):
     check_dense(gpu, *dense_case(m, n, k, seed=m + n + k), label=f"dense {m}x{n}x{k}")
