@@ -27,7 +27,7 @@ e4m3   exact 256-entry decode table, round-to-nearest-even saturating encoder
 e2m1   the FP4 codec (16 codes) and its two-per-byte packing
 quant  1x128 (activation) and 128x128 (weight) quantisers, FP8 and FP4
 gemm   dense, contiguous-grouped, masked-grouped and K-grouped reference GEMMs in fp64,
-       the BF16 and FP4 NT GEMMs; FC1 + SwiGLU on the masked layout
+       the BF16 and FP4 NT GEMMs; FC1 + SwiGLU on the masked and contiguous layouts
 check  the element-wise acceptance rule
 """
 
@@ -46,6 +46,8 @@ from .gemm import (  # noqa: F401
     fp4_gemm_nt_ref,
     masked_swiglu_quant_ref,
     masked_swiglu_ref,
+    contiguous_swiglu_quant_ref,
+    contiguous_swiglu_ref,
     silu,
 )
 from .check import tolerance_check, bf16_bits_to_float, bf16_round  # noqa: F401

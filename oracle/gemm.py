@@ -307,6 +307,41 @@ def masked_swiglu_quant_ref(qa, sfa, qb, sfb, masked_m):
     return hq, hs, valid
 
 
+def contiguous_swiglu_ref(qa, sfa, qb, sfb, m_indices):
+    """FC1 + SwiGLU on the contiguous layout (the prefill side of the same
+    MoE path; the popular-press article's section on MoE pairs the
+    contiguous layout with prefill and the masked one with decode), in fp64.
+    Reading as for the masked layout: B holds each expert's FC1 weight as
+    [gate; up], 2I rows, and h = silu(A . gate^T) * (A . up^T) for every row
+    with a valid expert tag.  Returns (h, valid): h is M x I with NaN in
+    padding rows."""
+    r, valid = grouped_contiguous_ref(qa, sfa, qb, sfb, m_indices)
+    i = qb.shape[1] // 2
+    if qb.shape[1] != 2 * i:
+        raise ValueError("B must hold gate and up halves of equal size")
+    return silu(r[:, :i]) * r[:, i:], valid
+
+
+def contiguous_swiglu_quant_ref(qa, sfa, qb, sfb, m_indices):
+    """Contiguous FC1 + SwiGLU with h quantised by the activation rule, as
+    the masked version does (one fp32 scale per row and 128-wide slab of I,
+    the decision in fp32 on fp32(h)).  Returns (hq, hs, valid): hq is M x I
+    e4m3 codes, hs is M x (I/128) fp32; padding rows hold code 0 and scale
+    NaN."""
+    from .quant import quantize_a_1x128
+
+    h, valid = contiguous_swiglu_ref(qa, sfa, qb, sfb, m_indices)
+    m, i = h.shape
+    if i % 128 != 0:
+        raise ValueError("I must be a multiple of 128")
+    hq = np.zeros((m, i), np.uint8)
+    hs = np.full((m, i // 128), np.nan, np.float32)
+    rows = np.nonzero(valid)[0]
+    if rows.size:
+        hq[rows], hs[rows] = quantize_a_1x128(h[rows].astype(np.float32))
+    return hq, hs, valid
+
+
 def fp4_gemm_nt_ref(pa, sfa, pb, sfb):
     """FP4 (e2m1) block-scaled NT GEMM in fp64: the dense FP8 method with
     e2m1 operands (the pages name FP4 as a GEMM format, pomoai.com, core

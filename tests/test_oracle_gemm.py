@@ -29,7 +29,8 @@ import torch
 
 from oracle import (gemm_nt_ref, gemm_nt_ref_at, grouped_contiguous_ref,
                     grouped_masked_ref, k_grouped_ref, k_grouped_ref_at, tolerance_check,
-                    bf16_gemm_nt_ref, bf16_to_f64, masked_swiglu_ref, masked_swiglu_quant_ref, silu)
+                    bf16_gemm_nt_ref, bf16_to_f64, masked_swiglu_ref, masked_swiglu_quant_ref, silu,
+                    contiguous_swiglu_ref, contiguous_swiglu_quant_ref)
 from oracle.gemm import grouped_contiguous_ref_at, grouped_masked_ref_at
 from oracle.e4m3 import decode_table
 
@@ -415,5 +416,94 @@ def test_swiglu_requantised_bounds():
     top = np.take_along_axis(np.abs(qv), np.argmax(np.abs(hv), axis=-1)[..., None], -1)
     assert np.all(top == 448.0)
     # and the scale is that element's magnitude over 448
+    amax = np.max(np.abs(hv), axis=-1)
+    assert np.allclose(sv, amax / 448.0, rtol=2.0 ** -22)
+
+
+def _swiglu_contig_case(up_code, gate_code=None, seed=47):
+    # the unit-up construction of _swiglu_case on the contiguous layout:
+    # expert tags with padding (-1) and an out-of-range tag (2 experts)
+    rng = np.random.default_rng(seed)
+    g, i, k = 2, 128, 256
+    tags = np.array([0, 0, 0, -1, 1, 1, 5, 1, -1, 0], np.int32)
+    m = tags.size
+    qa = random_codes(rng, (m, k))
+    sa = random_scales(rng, (m, k // 128))
+    qb = random_codes(rng, (g, 2 * i, k))
+    sb = random_scales(rng, (g, 2, k // 128))
+    if gate_code is not None:
+        qb[:, :i, :] = gate_code
+    qb[:, i:, :] = 0x00
+    qb[:, i:, 0] = up_code
+    qa[:, 0] = 0x38  # 1.0
+    sa[:, 0] = 1.0
+    sb[:, 1, 0] = 1.0
+    return qa, sa, qb, sb, tags, i
+
+
+def test_contiguous_swiglu_with_unit_up_is_silu_of_gate():
+    qa, sa, qb, sb, tags, i = _swiglu_contig_case(up_code=0x38)  # up = 1.0 exactly
+    h, valid = contiguous_swiglu_ref(qa, sa, qb, sb, tags)
+    assert valid.tolist() == [True, True, True, False, True, True, False, True, False, True]
+    # the gate half from the plain dense GEMM of each valid row with its expert
+    for r in np.nonzero(valid)[0]:
+        gate = gemm_nt_ref(qa[r:r + 1], sa[r:r + 1], qb[tags[r], :i], sb[tags[r], :1])[0]
+        ref = torch.nn.functional.silu(torch.from_numpy(gate)).numpy()
+        assert np.allclose(h[r], ref, rtol=1e-14, atol=0)
+    assert np.all(np.isnan(h[~valid]))
+    assert h.shape == (tags.size, i)
+
+
+def test_contiguous_swiglu_with_zero_gate_is_zero():
+    qa, sa, qb, sb, tags, i = _swiglu_contig_case(up_code=0x48, gate_code=0x00)  # gate = 0, up = 4
+    h, valid = contiguous_swiglu_ref(qa, sa, qb, sb, tags)
+    assert np.all(h[valid] == 0.0)
+
+
+def test_contiguous_swiglu_matches_the_masked_layout():
+    # the same rows and weights laid out both ways give the same h
+    rng = np.random.default_rng(53)
+    g, i, k = 3, 128, 384
+    counts = [5, 0, 9]
+    qb = random_codes(rng, (g, 2 * i, k))
+    sb = random_scales(rng, (g, 2, k // 128))
+    rows = [random_codes(rng, (c, k)) for c in counts]
+    srows = [random_scales(rng, (c, k // 128)) for c in counts]
+    max_m = max(counts)
+    qa_m = np.zeros((g, max_m, k), np.uint8)
+    sa_m = np.ones((g, max_m, k // 128), np.float32)
+    for e in range(g):
+        qa_m[e, :counts[e]], sa_m[e, :counts[e]] = rows[e], srows[e]
+    h_m, _ = masked_swiglu_ref(qa_m, sa_m, qb, sb, np.array(counts, np.int32))
+    qa_c = np.concatenate(rows)
+    sa_c = np.concatenate(srows)
+    tags = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)])
+    h_c, valid = contiguous_swiglu_ref(qa_c, sa_c, qb, sb, tags)
+    assert valid.all()
+    assert np.array_equal(h_c, np.concatenate([h_m[e, :counts[e]] for e in range(g)]))
+
+
+def test_contiguous_swiglu_requantised_bounds():
+    rng = np.random.default_rng(59)
+    g, i, k = 3, 256, 384
+    tags = np.array([0] * 7 + [-1] * 3 + [2] * 11 + [1] * 4, np.int32)
+    m = tags.size
+    qa = random_codes(rng, (m, k))
+    sa = random_scales(rng, (m, k // 128))
+    qb = random_codes(rng, (g, 2 * i, k))
+    sb = random_scales(rng, (g, 4, k // 128))
+    hq, hs, valid = contiguous_swiglu_quant_ref(qa, sa, qb, sb, tags)
+    h, _ = contiguous_swiglu_ref(qa, sa, qb, sb, tags)
+    assert hq.shape == (m, i) and hs.shape == (m, i // 128)
+    assert np.all(hq[~valid] == 0) and np.all(np.isnan(hs[~valid]))
+    vals = decode_table()[hq].astype(np.float64)
+    hv = h[valid].reshape(-1, i // 128, 128)
+    qv = vals[valid].reshape(-1, i // 128, 128)
+    sv = hs[valid].astype(np.float64)
+    deq = qv * sv[..., None]
+    bound = np.maximum(np.abs(hv) * 2.0 ** -4, sv[..., None] * 2.0 ** -10) * (1 + 2.0 ** -20)
+    assert np.all(np.abs(deq - hv) <= bound)
+    top = np.take_along_axis(np.abs(qv), np.argmax(np.abs(hv), axis=-1)[..., None], -1)
+    assert np.all(top == 448.0)
     amax = np.max(np.abs(hv), axis=-1)
     assert np.allclose(sv, amax / 448.0, rtol=2.0 ** -22)

@@ -46,6 +46,10 @@ MUTATIONS = [
     ("gemm.py", "return x / (1.0 + np.exp(-x))", "return x / (1.0 + np.exp(x))"),
     ("gemm.py", "hq[e, :rows], hs[e, :rows] = quantize_a_1x128(h[e, :rows].astype(np.float32))",
      "hq[e, :rows], hs[e, :rows] = quantize_a_1x128(np.abs(h[e, :rows]).astype(np.float32))"),
+    # contiguous SwiGLU: gate and up swapped, h of the wrong rows quantised
+    ("gemm.py", "return silu(r[:, :i]) * r[:, i:], valid", "return silu(r[:, i:]) * r[:, :i], valid"),
+    ("gemm.py", "hq[rows], hs[rows] = quantize_a_1x128(h[rows].astype(np.float32))",
+     "hq[rows], hs[rows] = quantize_a_1x128(h[rows[::-1]].astype(np.float32))"),
     # BF16: wrong half of the fp32 word, transposed operand
     ("gemm.py", "b = np.asarray(bits, np.uint16).astype(np.uint32) << 16", "b = np.asarray(bits, np.uint16).astype(np.uint32) << 15"),
     ("gemm.py", "    return a @ b.T\n", "    return a @ b[::-1].T\n"),
