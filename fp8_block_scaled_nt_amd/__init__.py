@@ -29,7 +29,8 @@ LIB_PATH = os.environ.get("DG_LIBRARY") or os.path.join(_PKG_DIR, "libdg.so")
 
 __all__ = [
     "DGError", "lib", "fp8_gemm_nt", "fp8_gemm_nt_noalloc", "m_grouped_fp8_gemm_nt_contiguous",
-    "m_grouped_fp8_gemm_nt_masked", "m_grouped_fp8_gemm_nt_masked_swiglu", "quantize_a_1x128", "quantize_b_128x128",
+    "m_grouped_fp8_gemm_nt_masked", "m_grouped_fp8_gemm_nt_masked_swiglu", "m_grouped_fp8_gemm_nt_contiguous_swiglu",
+    "quantize_a_1x128", "quantize_b_128x128",
     "k_grouped_fp8_gemm_nt", "bf16_gemm_nt", "fp4_gemm_nt", "quantize_a_1x128_fp4", "quantize_b_128x128_fp4", "get_m_alignment_for_contiguous_layout", "get_sfa_ld", "empty_sfa",
     "profile_next_launch",
     "reserve_workspace", "dense_workspace_size",
@@ -52,6 +53,7 @@ _SIGNATURES = {
     "dg_m_grouped_fp8_gemm_nt_contiguous": [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _vp],
     "dg_m_grouped_fp8_gemm_nt_masked": [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _vp],
     "dg_m_grouped_fp8_gemm_nt_masked_swiglu": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _vp],
+    "dg_m_grouped_fp8_gemm_nt_contiguous_swiglu": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _vp],
     "dg_k_grouped_fp8_gemm_nt": [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _vp],
     "dg_bf16_gemm_nt": [_vp, _vp, _vp, _ci, _ci, _ci, _vp],
     "dg_fp4_gemm_nt": [_vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _vp],
@@ -275,6 +277,36 @@ def m_grouped_fp8_gemm_nt_masked_swiglu(a_pair, b_pair, h_pair, masked_m, expect
     _check(lib().dg_m_grouped_fp8_gemm_nt_masked_swiglu(
         _ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(hq), _ptr(hs), _ptr(masked_m), g, max_m, inter, k,
         int(expected_m), _stream()))
+    return hq, hs
+
+
+def m_grouped_fp8_gemm_nt_contiguous_swiglu(a_pair, b_pair, h_pair, m_indices):
+    """MoE FC1 + SwiGLU on the contiguous layout: B is [g, 2*inter, k] holding
+    each expert's gate rows, then its up rows; h = silu(gate) * up of every
+    row with a valid tag is written as e4m3 codes hq [m, inter] with 1x128
+    fp32 scales hs [inter/128, get_sfa_ld(m)], the A operand layout of the
+    contiguous GEMM."""
+    a, sfa = a_pair
+    b, sfb = b_pair
+    hq, hs = h_pair
+    _need(a, "a", _FP8, 2)
+    _need(b, "b", _FP8, 3)
+    _need(hq, "hq", _FP8, 2)
+    _need(sfa, "sfa", (torch.float32,), 2)
+    _need(sfb, "sfb", (torch.float32,), 3)
+    _need(hs, "hs", (torch.float32,), 2)
+    _need(m_indices, "m_indices", (torch.int32,), 1)
+    m, k = a.shape
+    g = b.shape[0]
+    inter = b.shape[1] // 2
+    if b.shape[2] != k or b.shape[1] != 2 * inter or m_indices.numel() != m:
+        raise ValueError("shape mismatch")
+    if tuple(hq.shape) != (m, inter) or tuple(hs.shape) != (inter // 128, get_sfa_ld(m)):
+        raise ValueError("output shape mismatch")
+    if tuple(sfa.shape) != (k // 128, get_sfa_ld(m)) or tuple(sfb.shape) != (g, (2 * inter + 127) // 128, k // 128):
+        raise ValueError("scale shape mismatch")
+    _check(lib().dg_m_grouped_fp8_gemm_nt_contiguous_swiglu(
+        _ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(hq), _ptr(hs), _ptr(m_indices), m, inter, k, g, _stream()))
     return hq, hs
 
 

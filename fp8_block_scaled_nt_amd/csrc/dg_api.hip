@@ -161,6 +161,13 @@ const Config* configs(int* count) {
       make_config<256, 256, 2, 4, 2, dg::kMasked, dg::kInterleaved, dg::kFp8, dg::kEpiSwigluFp8>("swiglu_256x256_w8_s2"),
       make_config<128, 256, 2, 4, 3, dg::kMasked, dg::kInterleaved, dg::kFp8, dg::kEpiSwigluFp8>("swiglu_128x256_w8_s3"),
       make_config<64, 256, 1, 4, 3, dg::kMasked, dg::kInterleaved, dg::kFp8, dg::kEpiSwigluFp8>("swiglu_64x256_w4_s3"),
+      // the same on the contiguous layout (tile rows within the 128-row alignment)
+      make_config<128, 256, 1, 4, 2, dg::kContiguous, dg::kSingleB, dg::kFp8, dg::kEpiSwigluFp8>(
+          "swiglu_contig_128x256_w4_s2_sb"),
+      make_config<128, 256, 2, 4, 3, dg::kContiguous, dg::kInterleaved, dg::kFp8, dg::kEpiSwigluFp8>(
+          "swiglu_contig_128x256_w8_s3"),
+      make_config<64, 256, 1, 4, 3, dg::kContiguous, dg::kInterleaved, dg::kFp8, dg::kEpiSwigluFp8>(
+          "swiglu_contig_64x256_w4_s3"),
   };
   *count = sizeof(table) / sizeof(table[0]);
   return table;
@@ -1135,6 +1142,48 @@ int dg_m_grouped_fp8_gemm_nt_masked_swiglu(const uint8_t* a, const float* sfa, c
   fill_common(p, *c, max_m, 2 * inter, k);
   p.tiles_n = inter / 128;  // one tile per 128 h columns (128 gate + 128 up rows of B)
   if (int s = set_num_tiles(p, num_groups)) return s;
+  return launch(*c, p, p.num_tiles, (hipStream_t)stream);
+}
+
+int dg_m_grouped_fp8_gemm_nt_contiguous_swiglu(const uint8_t* a, const float* sfa, const uint8_t* b,
+                                               const float* sfb, uint8_t* hq, float* hs, const int32_t* m_indices,
+                                               int m, int inter, int k, int num_groups, dg_stream_t stream) {
+  if (!a || !sfa || !b || !sfb || !hq || !hs || !m_indices)
+    return fail(DG_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (m < 0) return fail(DG_ERR_INVALID_ARGUMENT, "m must be >= 0 (got %d)", m);
+  if (num_groups < 1) return fail(DG_ERR_INVALID_ARGUMENT, "num_groups must be >= 1 (got %d)", num_groups);
+  if (inter < 128 || inter % 128 != 0 || inter > (1 << 29))
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "inter must be a positive multiple of 128 (got %d)", inter);
+  if (int s = check_k_n(2 * inter, k)) return s;
+  if (m % 128 != 0)
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "m must be a multiple of the 128-row alignment (got %d)", m);
+  if (int s = check_rows(m, k)) return s;
+  if ((long long)m * inter > 0xFFFFFFFFLL) return fail(DG_ERR_UNSUPPORTED_SHAPE, "h must stay below 4 GiB");
+  if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(hq) || !aligned16(hs) ||
+      (reinterpret_cast<uintptr_t>(m_indices) & 3u))
+    return fail(DG_ERR_MISALIGNED, "pointers must be 16-byte aligned (m_indices 4-byte)");
+  if (m == 0) return ok();
+  int dev;
+  DeviceInfo* info;
+  if (int s = current_device(&dev, &info)) return s;
+  const Config* c;
+  if (int s = forced_config(dg::kContiguous, &c, dg::kFp8, dg::kEpiSwigluFp8)) return s;
+  if (!c) {
+    // the contiguous GEMM's rule on its 256-column tiles
+    const long long tiles = (long long)(m / 128) * (inter / 128);
+    const long long t128 = 2 * tiles;
+    c = find_config(t128 <= 128        ? "swiglu_contig_64x256_w4_s3"
+                    : tiles >= info->cus ? "swiglu_contig_128x256_w4_s2_sb"
+                                         : "swiglu_contig_128x256_w8_s3",
+                    dg::kContiguous, dg::kFp8, dg::kEpiSwigluFp8);
+  }
+  dg::GemmParams p{};
+  p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.m_indices = m_indices;
+  p.hq = hq; p.hs = hs; p.inter = inter;
+  p.num_groups = num_groups;
+  fill_common(p, *c, m, 2 * inter, k);
+  p.tiles_n = inter / 128;  // one tile per 128 h columns (128 gate + 128 up rows of B)
+  if (int s = set_num_tiles(p, 1)) return s;
   return launch(*c, p, p.num_tiles, (hipStream_t)stream);
 }
 

@@ -36,7 +36,7 @@
 // element i is row 4*(l/16) + i, column l % 16 of the 16x16 fragment.  The
 // same kernel also runs bf16 operands (no scales) and e2m1 operands (FP4,
 // block scales), and a SwiGLU + FP8 requantisation epilogue on the masked
-// layout.
+// and contiguous layouts.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -62,7 +62,7 @@ enum Variant { kDense = 0, kContiguous = 1, kMasked = 2, kKGrouped = 3 };
 // (a 128-byte slab row then holds 256 K values: two scale slabs).
 enum DType { kFp8 = 0, kBf16 = 1, kFp4 = 2 };
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-// Epilogue: store D as bf16, or (MoE FC1 on the masked layout) pair each
+// Epilogue: store D as bf16, or (MoE FC1 on the masked or contiguous layout) pair each
 // gate column with its up column, apply SwiGLU and quantise h with the 1 x 128
 // activation rule, so the second GEMM reads h as FP8 without a round trip.
 enum Epilogue { kEpiBf16 = 0, kEpiSwigluFp8 = 1 };
@@ -84,8 +84,8 @@ struct GemmParams {
   const int32_t* m_indices;  // contiguous layout
   const int32_t* masked_m;   // masked layout
   const int32_t* k_sizes;    // K-grouped layout: K columns of each group
-  uint8_t* hq;               // SwiGLU epilogue: h codes [groups][m][inter]
-  float* hs;                 // SwiGLU epilogue: h scales [groups][inter/128][sfa_ld]
+  uint8_t* hq;               // SwiGLU epilogue: h codes [groups][m][inter] (contiguous: [m][inter])
+  float* hs;                 // SwiGLU epilogue: h scales [groups][inter/128][sfa_ld] (contiguous: one group)
   int inter;                 // SwiGLU epilogue: I (B holds 2I rows: gate, then up)
   int m;                     // rows of A (dense, contiguous) or max_m (masked)
   int n;
@@ -357,7 +357,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   // SwiGLU: a tile covers 128 h columns (one activation scale block), each
   // wave TN / 2 of them: its first TN / 2 tile columns are gate rows of B and
   // its last TN / 2 the matching up rows, so gate and up meet in one lane.
-  static_assert(EPI == kEpiBf16 || (VAR == kMasked && DT == kFp8 && BN == 256 && TN % 32 == 0),
+  static_assert(EPI == kEpiBf16 ||
+                    ((VAR == kMasked || VAR == kContiguous) && DT == kFp8 && BN == 256 && TN % 32 == 0),
                 "SwiGLU epilogue shape");
   static_assert(DT != kFp4 || (VAR == kDense && SCHED != kPingPong && EPI == kEpiBf16),
                 "the FP4 path is the dense interleaved GEMM");
@@ -967,8 +968,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
     // tile row (through LDS).  One thread per tile row then forms the row's
     // scale and its reciprocal, and the waves quantise their h values with
     // them.  Codes are staged in LDS and leave as 16-byte row stores; scales
-    // go to the slab-major layout the masked GEMM reads its A scales from.
-    // Rows past the expert's count are not written.
+    // go to the slab-major layout the masked (contiguous) GEMM reads its A
+    // scales from.  Rows past the expert's count (contiguous: rows that do
+    // not carry the tile's expert tag) are not written.
     constexpr int FH = FN / 2;
     constexpr int kHalf = TN / 2;             // h columns per wave
     constexpr int kCodePitch = BN / 2 + 16;   // bytes per staged code row
@@ -1023,7 +1025,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
       y = __builtin_fmaf(__builtin_fmaf(-sc, y, 1.f), y, y);
       s_sc[rl] = sc;
       s_rc[rl] = y;
-      if (m0 + rl < valid_rows) p.hs[((size_t)g * (p.inter >> 7) + tn) * p.sfa_ld + m0 + rl] = sc;
+      // (contiguous: g is 0, h rows are the rows of A; rows of another
+      // expert's tag or padding get nothing)
+      if (m0 + rl < valid_rows && (VAR != kContiguous || s_row_ok[rl]))
+        p.hs[((size_t)g * (p.inter >> 7) + tn) * p.sfa_ld + m0 + rl] = sc;
     }
     block_barrier();
     #pragma unroll
@@ -1054,6 +1059,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
     for (int idx = threadIdx.x; idx < BM * kChunks; idx += kThreads) {
       const int rl = idx / kChunks, ch = idx % kChunks;
       if (rl >= rows_here) break;
+      if (VAR == kContiguous && !s_row_ok[rl]) continue;
       *(v4i*)(HQ + (size_t)(m0 + rl) * p.inter + ch * 16) = *(const v4i*)(s_code + rl * kCodePitch + ch * 16);
     }
     return;

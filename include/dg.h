@@ -193,6 +193,37 @@ int dg_m_grouped_fp8_gemm_nt_masked_swiglu(const uint8_t* a, const float* sfa, c
                                            int max_m, int inter, int k, int expected_m, dg_stream_t stream);
 
 /*
+ * MoE FC1 + SwiGLU + FP8 requantisation on the contiguous layout: the
+ * prefill side of dg_m_grouped_fp8_gemm_nt_masked_swiglu (the popular-press
+ * article on DeepGEMM, yeyulingfeng.com, section on MoE: the contiguous
+ * layout for prefill, the masked one for decode; section 04 on Mega MoE for
+ * the fused FC1 and SwiGLU).  B holds each expert's FC1 weight as [gate; up]
+ * as for the masked entry point, and for every row m whose tag
+ * e = m_indices[m] lies in [0, num_groups):
+ *
+ *   gate[j] = FP8 GEMM of A[m] with B[e][j]           (as dg_m_grouped_fp8_gemm_nt_contiguous,
+ *   up[j]   = FP8 GEMM of A[m] with B[e][inter + j]    but kept in fp32)
+ *   h[j]    = silu(gate[j]) * up[j]
+ *
+ * quantised with the activation rule of dg_quantize_a_1x128, all in fp32.
+ * Layouts:
+ *     A   [m][k] e4m3, sfa [k/128][dg_get_sfa_ld(m)], m_indices [m] (-1 = padding)
+ *     B   [num_groups][2*inter][k] e4m3, sfb [num_groups][2*inter/128][k/128]
+ *     hq  [m][inter] e4m3 codes (output)
+ *     hs  [inter/128][dg_get_sfa_ld(m)] fp32 scales (output)
+ * hq and hs are exactly the A operand of a contiguous GEMM with k = inter
+ * and the same m_indices.  m must be a multiple of the 128-row alignment
+ * (every 128-row block holds one expert's rows and padding); inter a
+ * positive multiple of 128, k of 128; pointers 16-byte aligned (m_indices
+ * 4-byte).  Padding rows, rows with an out-of-range tag and the padding
+ * entries of hs are left untouched.  Errors as for the other entry points;
+ * nothing is allocated.
+ */
+int dg_m_grouped_fp8_gemm_nt_contiguous_swiglu(const uint8_t* a, const float* sfa, const uint8_t* b,
+                                               const float* sfb, uint8_t* hq, float* hs, const int32_t* m_indices,
+                                               int m, int inter, int k, int num_groups, dg_stream_t stream);
+
+/*
  * BF16 NT GEMM: D[m][n] = bf16( sum_k A[m, k] * B[n, k] ) for bf16 A [m][k]
  * and B [n][k] (bit patterns in uint16), fp32 accumulation, no scales
  * ("DeepGEMM: making LLM matrix multiplication fly", pomoai.com, core

@@ -172,6 +172,30 @@ def run_swiglu(qa, sa, qb, sb, masked_m, dev, expected_m=0, guard=256):
             hq_flat, hs_flat)
 
 
+def run_contig_swiglu(qa, sa, qb, sb, m_indices, dev, guard=256):
+    """Fused FC1 + SwiGLU + requantisation on the contiguous layout.  Returns
+    (hq, hs, hq_flat, hs_flat): hq as uint8 [m][inter], hs as raw uint32 bits
+    in the device layout [inter/128][ld], and the whole prefilled buffers."""
+    m, k = qa.shape
+    inter = qb.shape[1] // 2
+    ld = sfa_ld(m)
+    a = codes_to_device(qa, dev)
+    b = codes_to_device(qb, dev)
+    sfa = f32_to_device(slab_major(sa), dev)
+    sfb = f32_to_device(sb, dev)
+    idx = torch.from_numpy(np.asarray(m_indices, np.int32)).to(dev)
+    nq = m * inter
+    ns = (inter // 128) * ld
+    hq_flat = torch.full((nq + guard,), SENTINEL_CODE, dtype=torch.uint8, device=dev)
+    hs_flat = torch.full((ns + guard,), SENTINEL_SCALE, dtype=torch.int32, device=dev)
+    hq = hq_flat[:nq].view(m, inter)
+    hs = hs_flat[:ns].view(torch.float32).view(inter // 128, ld)
+    dg.m_grouped_fp8_gemm_nt_contiguous_swiglu((a, sfa), (b, sfb), (hq.view(torch.float8_e4m3fn), hs), idx)
+    torch.cuda.synchronize()
+    return (hq.cpu().numpy(), hs_flat[:ns].view(inter // 128, ld).cpu().numpy().view(np.uint32),
+            hq_flat, hs_flat)
+
+
 def swiglu_guards_untouched(hq_flat, hs_flat, nq, ns):
     tq = hq_flat[nq:].cpu().numpy()
     ts = hs_flat[ns:].cpu().numpy().view(np.uint32)

@@ -99,6 +99,20 @@ def test_swiglu_validation(lib):
     assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 4, 0, 256, 256, 0, None) == 0    # max_m = 0: no-op
 
 
+def test_contiguous_swiglu_validation(lib):
+    f = lib.dg_m_grouped_fp8_gemm_nt_contiguous_swiglu
+    #       a     sfa   b     sfb   hq    hs    m_indices   m  inter  k  groups
+    assert f(GOOD, GOOD, GOOD, GOOD, None, GOOD, GOOD, 128, 256, 256, 4, None) == 1   # null hq
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, -128, 256, 256, 4, None) == 1  # negative m
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 128, 256, 256, 0, None) == 1   # no groups
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 100, 256, 256, 4, None) == 2   # m not 128-aligned
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 128, 192, 256, 4, None) == 2   # inter not whole blocks
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 128, 256, 200, 4, None) == 2   # k not whole slabs
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, ODD, GOOD, 128, 256, 256, 4, None) == 3    # misaligned hs
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, P(0x10002), 128, 256, 256, 4, None) == 3
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 0, 256, 256, 4, None) == 0     # m = 0: no-op
+
+
 def test_bf16_validation(lib):
     f = lib.dg_bf16_gemm_nt
     assert f(None, GOOD, GOOD, 64, 64, 128, None) == 1      # null a
