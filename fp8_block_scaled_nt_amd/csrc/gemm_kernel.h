@@ -99,6 +99,8 @@ struct GemmParams {
   int tiles_n;
   int num_tiles;
   int group_m;               // raster group height in tiles
+  int b_stream;              // 1: every B byte is read by one tile only (one row block
+                             // of tiles): B's LDS DMA carries the non-temporal hint
   // split-K (dense): each tile's K slabs are shared by `splits` workgroups of
   // `split_slabs` slabs each; their fp32 partial tiles meet in a workspace and
   // the last workgroup to arrive adds them in split order and stores D.
@@ -171,6 +173,15 @@ constexpr int kVmPerDma = 2;  // vmcnt events per lds_dma16 / lds_dma4: the EXEC
 __device__ __forceinline__ void lds_dma16(v4i_rsrc rs, uint32_t voff, uint32_t soff, void* lds_dst) {
   uint64_t exec_save;
   asm volatile(DG_M0_GUARD "s_mov_b32 m0, %4\n\ts_mov_b64 exec, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               : "=&s"(exec_save) : "v"(voff), "s"(rs), "s"(soff), "s"(lds_addr(lds_dst)) : "memory", "m0", "scc");
+}
+
+// The same with the non-temporal hint, for operand bytes read exactly once
+// (B of a launch whose tiles all share one row block): they then do not
+// push the rows every tile re-reads (A) out of the XCD's L2.
+__device__ __forceinline__ void lds_dma16_stream(v4i_rsrc rs, uint32_t voff, uint32_t soff, void* lds_dst) {
+  uint64_t exec_save;
+  asm volatile(DG_M0_GUARD "s_mov_b32 m0, %4\n\ts_mov_b64 exec, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
                : "=&s"(exec_save) : "v"(voff), "s"(rs), "s"(soff), "s"(lds_addr(lds_dst)) : "memory", "m0", "scc");
 }
 
@@ -584,7 +595,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
       const int jj = d - kPerWaveA;
       const int j = jj * kWaves + wave;
       if (kJb % kWaves != 0 && j >= kJb) return;
-      lds_dma16(rs_b, b_off[jj], (uint32_t)kb * kSlab, (kSB ? smem + S::kBShared : st + S::kA) + j * kDmaBytes);
+      uint8_t* dst = (kSB ? smem + S::kBShared : st + S::kA) + j * kDmaBytes;
+      if (p.b_stream) lds_dma16_stream(rs_b, b_off[jj], (uint32_t)kb * kSlab, dst);
+      else lds_dma16(rs_b, b_off[jj], (uint32_t)kb * kSlab, dst);
     } else {
       const int e = d - kPerWaveA - kPerWaveB;
       const int h = e >> 1;                 // scale slab of this slab
@@ -1068,8 +1081,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   // ---- split-K fix-up: publish this split's partial tile; the last split
   // to arrive adds all partials in split order (deterministic) and goes on to
   // store D.  Partials are laid out fragment-native (each lane owns 16
-  // contiguous bytes per fragment).  The reducer reads kChunk splits'
-  // partials per batch; loads past the last split return zero.
+  // contiguous bytes per fragment).  The reducer reads up to kChunk splits'
+  // partials per batch, issuing loads for existing splits only.
   //
   // Why the hand-off is ordered across the per-XCD L2s without a release /
   // acquire pair: the partial stores and the reducer's loads carry SC1, the
@@ -1087,7 +1100,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   // which measured twice as slow as these coherent accesses on decode shapes.
   if constexpr (VAR == kDense && SCHED != kPingPong) if (p.splits > 1) {
     constexpr int kTileFloats = BM * BN;
-    constexpr int kChunk = (FM * FN * 4) >= 128 ? 1 : 128 / (FM * FN * 4);
+    constexpr int kChunkMax = (FM * FN * 4) >= 128 ? 1 : 128 / (FM * FN * 4);
+    constexpr int kChunk = kChunkMax > 8 ? 8 : kChunkMax;
     float* part = p.ws_partial + (size_t)tile_id * p.splits * kTileFloats;
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(part, 0, p.splits * kTileFloats * 4, kBufferRsrcWord3);
@@ -1116,9 +1130,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
         #pragma unroll
         for (int i = 0; i < FM; ++i)
           #pragma unroll
-          for (int j = 0; j < FN; ++j)
-            part_v[c][i][j] = __builtin_amdgcn_raw_buffer_load_b128(
-                rs, ((sp0 + c) * kTileFloats + (((wave * FM + i) * FN + j) * 64 + lane) * 4) * 4, 0, kCpolSc1);
+          for (int j = 0; j < FN; ++j) {
+            // only the splits that exist: a load past the last one would
+            // return zero but still cost its trip through the texture path
+            part_v[c][i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+            if (sp0 + c < p.splits)
+              part_v[c][i][j] = __builtin_amdgcn_raw_buffer_load_b128(
+                  rs, ((sp0 + c) * kTileFloats + (((wave * FM + i) * FN + j) * 64 + lane) * 4) * 4, 0, kCpolSc1);
+          }
       #pragma unroll
       for (int c = 0; c < kChunk; ++c)
         #pragma unroll
