@@ -305,6 +305,7 @@ def test_dense_long_k_pipeline(gpu):
     (1, 64, 512, "4"),
     (64, 130, 896, "7"),      # one slab per split
     (100, 192, 768, "2"),     # two tile rows
+    (64, 130, 1408, "11"),    # more splits than one batch of the reducer's partial loads
 ])
 @pytest.mark.parametrize("cfg", ["dense_64x64_w4_s8", "dense_64x32_w4_s4", "dense_128x128_w4_s2",
                                  "dense_128x256_w4_s2_sb"])
