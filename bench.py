@@ -344,6 +344,30 @@ def setup_workload(torch, np, dg, W, name, dev):
             dg.k_grouped_fp8_gemm_nt((st["qa"], st["sfa"]), (st["qb"], st["sfb"]), st["d"], st["ks"])
 
         return w.kind, dict(k_sizes=inp["k_sizes"], m=m, n=n, k=k), rot, launch, None, inp
+    if w.kind == "swiglu_contig":
+        inter, k = s["inter"], s["k"]
+        idx = torch.from_numpy(inp["m_indices"]).to(dev)
+        m = idx.numel()
+        qa, sfa = dg.quantize_a_1x128(torch.from_numpy(inp["a"]).to(dev))
+        qb, sfb = dg.quantize_b_128x128(torch.from_numpy(inp["b"]).to(dev))
+        ld = dg.get_sfa_ld(m)
+
+        def make(i):
+            hq = torch.empty((m, inter), dtype=torch.float8_e4m3fn, device=dev)
+            hs = torch.empty((inter // 128, ld), dtype=torch.float32, device=dev)
+            if i == 0:
+                return {"qa": qa, "sfa": sfa, "qb": qb, "sfb": sfb, "hq": hq, "hs": hs, "idx": idx}
+            return {"qa": qa.clone(), "sfa": sfa.clone(), "qb": qb.clone(), "sfb": sfb.clone(), "hq": hq,
+                    "hs": hs, "idx": idx.clone()}
+
+        rot = Rotation(make, qa.numel() + qb.numel() + m * inter)
+
+        def launch(st):
+            dg.m_grouped_fp8_gemm_nt_contiguous_swiglu((st["qa"], st["sfa"]), (st["qb"], st["sfb"]),
+                                                       (st["hq"], st["hs"]), st["idx"])
+
+        return (w.kind, dict(m_indices=inp["m_indices"], g=len(s["group_rows"]), n=2 * inter, k=k), rot, launch,
+                None, inp)
     if w.kind == "swiglu":
         g, max_m, inter, k = s["g"], s["max_m"], s["inter"], s["k"]
         mm = torch.from_numpy(inp["masked_m"]).to(dev)

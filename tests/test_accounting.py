@@ -44,6 +44,10 @@ def test_named_workload_sizes():
     # codes (1 byte x 2048) plus one fp32 scale per 128 of them
     f2, b2 = W.workload_work("moe_swiglu_16x256_i2048_k7168")
     assert f2 == f and b2 == b - 2067 * 4096 * 2 + 2067 * 2048 + 2067 * 16 * 4
+    # the same exchange on the contiguous layout's 32768 tagged rows
+    f, b = W.workload_work("moe_contiguous_4x8192_n4096_k7168")
+    f2, b2 = W.workload_work("moe_swiglu_contig_4x8192_i2048_k7168")
+    assert f2 == f and b2 == b - 32768 * 4096 * 2 + 32768 * 2048 + 32768 * 16 * 4
 
 
 def test_masked_draw_recipe():

@@ -172,3 +172,61 @@ def test_feeds_the_contiguous_gemm(gpu):
         assert np.all(err <= rule + bound), (e, float(np.max(err - rule - bound)))
         res = oracle.tolerance_check(d2[rows[sel]], r2[rows[sel]], rms=rms2)
         print(f"  expert {e}: {res['n_bad']} of {res['n']} outside the plain GEMM rule", flush=True)
+
+
+def test_full_size_sampled(gpu):
+    """The contiguous FC1 workload (4 experts x 8192 rows, 2I = 4096, I = 2048,
+    K = 7168), run as the benchmark runs it: quantised on the GPU by the
+    library, the fused kernel at its default configuration.  Every h code and
+    scale of the tagged rows is written (no row is padding here) and the guard
+    bands keep their sentinels; for each expert the oracle re-quantises three
+    of its A rows and its B on the CPU (the codes and scales must be
+    bit-identical) and computes h for those rows."""
+    import torch
+
+    import fp8_block_scaled_nt_amd as dg
+    name = "moe_swiglu_contig_4x8192_i2048_k7168"
+    x = W.draw(name)
+    s = W.WORKLOADS[name].shape
+    inter, k, g = s["inter"], s["k"], len(s["group_rows"])
+    idx = np.asarray(x["m_indices"], np.int32)
+    m = idx.size
+    print(f"[case] contiguous swiglu full size {name}", flush=True)
+    qa, sfa = dg.quantize_a_1x128(H.f32_to_device(x["a"], gpu))
+    qb, sfb = dg.quantize_b_128x128(H.f32_to_device(x["b"], gpu))
+    ld = H.sfa_ld(m)
+    nq, ns, guard = m * inter, (inter // 128) * ld, 4096
+    fq = torch.full((nq + guard,), H.SENTINEL_CODE, dtype=torch.uint8, device=gpu)
+    fs = torch.full((ns + guard,), H.SENTINEL_SCALE, dtype=torch.int32, device=gpu)
+    hq_t = fq[:nq].view(m, inter)
+    hs_t = fs[:ns].view(torch.float32).view(inter // 128, ld)
+    dg.m_grouped_fp8_gemm_nt_contiguous_swiglu((qa, sfa), (qb, sfb), (hq_t.view(torch.float8_e4m3fn), hs_t),
+                                               torch.from_numpy(idx).to(gpu))
+    torch.cuda.synchronize()
+    assert H.swiglu_guards_untouched(fq, fs, nq, ns)
+    # no row is padding: every h code and every row's scales are written
+    assert not bool((hq_t == H.SENTINEL_CODE).any())
+    assert not bool((hs_t[:, :m].view(torch.int32) == H.SENTINEL_SCALE).any())
+    hq = hq_t.cpu().numpy()
+    hs = fs[:ns].view(inter // 128, ld).cpu().numpy().view(np.uint32)
+    rng = np.random.default_rng(131)
+    fixed, total, same = 0, 0, 0
+    for e in range(g):
+        seg = np.nonzero(idx == e)[0]
+        rows = np.unique(np.concatenate([[seg[0], seg[-1]], rng.choice(seg, 1)]))
+        qa_r, sa_r = oracle.quantize_a_1x128(x["a"][rows])
+        assert np.array_equal(qa.view(torch.uint8)[torch.from_numpy(rows).to(gpu)].cpu().numpy(), qa_r)
+        qb_e, sb_e = oracle.quantize_b_128x128(x["b"][e])
+        assert np.array_equal(qb[e].view(torch.uint8).cpu().numpy(), qb_e)
+        assert np.array_equal(sfb[e].cpu().numpy(), sb_e)
+        sub = oracle.gemm_nt_ref(qa_r, sa_r, qb_e, sb_e)
+        gate, up = sub[:, :inter], sub[:, inter:]
+        h = oracle.silu(gate) * up
+        f, t = check_rows(hq[rows], np.ascontiguousarray(hs[:, rows].T), h,
+                          rule_tol(gate, up, rms(gate), rms(up)), f"{name} expert {e}")
+        fixed, total = fixed + f, total + t
+        hq_o, _ = oracle.quantize_a_1x128(h.astype(np.float32))
+        same += int(np.sum(T[hq[rows]] == T[hq_o]))
+    print(f"  fixed {fixed / max(total, 1):.5f} same code as the oracle {same / max(total, 1):.5f} of {total}",
+          flush=True)
+    assert fixed >= 0.1 * total and same >= 0.98 * total

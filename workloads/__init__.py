@@ -23,7 +23,7 @@ class Workload:
 
     def __init__(self, name, kind, desc, **shape):
         self.name = name
-        self.kind = kind  # "dense" | "contiguous" | "masked" | "kgrouped" | "bf16" | "swiglu" | "fp4"
+        self.kind = kind  # "dense" | "contiguous" | "masked" | "kgrouped" | "bf16" | "swiglu" | "swiglu_contig" | "fp4"
         self.desc = desc
         self.shape = shape
 
@@ -86,6 +86,14 @@ WORKLOADS = {
         "moe_swiglu_16x256_c64_i2048_k7168", "swiglu",
         "MoE FC1 + SwiGLU + requantise, masked layout, 16 experts, max_m=256, counts U{0..64}, I=2048 K=7168",
         g=16, max_m=256, inter=2048, k=7168, b_std=0.02, count_hi=64),
+    # MoE FC1 + SwiGLU + FP8 requantisation on the contiguous (prefill)
+    # layout: the contiguous shape read as [gate; up] (2I = 4096 rows,
+    # I = 2048), drawn with the same seed, so its inputs equal the contiguous
+    # workload's
+    "moe_swiglu_contig_4x8192_i2048_k7168": Workload(
+        "moe_swiglu_contig_4x8192_i2048_k7168", "swiglu_contig",
+        "MoE FC1 + SwiGLU + requantise, contiguous layout, 4 experts x 8192 rows, I=2048 K=7168",
+        group_rows=(8192, 8192, 8192, 8192), inter=2048, k=7168, b_std=0.02),
     # BF16 dense GEMM on the large dense shape (operands rounded to bf16 by
     # the caller from these fp32 draws)
     "bf16_dense_4096x7168x16384": Workload(
@@ -173,6 +181,8 @@ def draw(name, seed=0):
         return draw_dense(s["m"], s["n"], s["k"], seed, s["b_std"])
     if w.kind == "contiguous":
         return draw_contiguous(s["group_rows"], s["n"], s["k"], seed, s["b_std"])
+    if w.kind == "swiglu_contig":
+        return draw_contiguous(s["group_rows"], 2 * s["inter"], s["k"], seed, s["b_std"])
     if w.kind == "kgrouped":
         return draw_kgrouped(s["k_sizes"], s["m"], s["n"], seed, s["b_std"])
     if w.kind == "swiglu":
@@ -218,6 +228,19 @@ def algorithmic_work(kind, **p):
         nbytes = (rows * k + 4 * rows * kb + experts * (n * k + 4 * nb * kb) + 4 * cnt.size
                   + rows * i + 4 * rows * (i // SLAB))
         return flops, nbytes
+    elif kind == "swiglu_contig":
+        # the contiguous FC1 GEMM with n = 2I, writing h for the tagged rows
+        # as e4m3 codes (1 byte) with one fp32 scale per 128 columns
+        m_indices = np.asarray(p["m_indices"])
+        g = p["g"]
+        ok = (m_indices >= 0) & (m_indices < g)
+        rows = int(ok.sum())
+        experts = int(np.unique(m_indices[ok]).size)
+        i = n // 2
+        flops = 2.0 * rows * n * k
+        nbytes = (rows * k + 4 * rows * kb + experts * (n * k + 4 * nb * kb) + 4 * m_indices.size
+                  + rows * i + 4 * rows * (i // SLAB))
+        return flops, nbytes
     elif kind == "fp4":
         # half a byte per element of A and B, their fp32 scales, bf16 D
         m = p["m"]
@@ -253,6 +276,9 @@ def workload_work(name, inputs=None):
     if w.kind == "contiguous":
         mi = inputs["m_indices"] if inputs is not None else contiguous_indices(s["group_rows"])
         return algorithmic_work("contiguous", m_indices=mi, g=len(s["group_rows"]), n=s["n"], k=s["k"])
+    if w.kind == "swiglu_contig":
+        mi = inputs["m_indices"] if inputs is not None else contiguous_indices(s["group_rows"])
+        return algorithmic_work("swiglu_contig", m_indices=mi, g=len(s["group_rows"]), n=2 * s["inter"], k=s["k"])
     if w.kind in ("bf16", "fp4"):
         return algorithmic_work(w.kind, m=s["m"], n=s["n"], k=s["k"])
     if w.kind == "kgrouped":
