@@ -662,7 +662,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(MAIN_WORKLOAD),
-                "kernel": "gemm_fp8_nt_kernel<64, 32, 2, 2, 4> (dense fp8, 64 x 32 tiles, split-K 7)",
+                "kernel": "gemm_fp8_nt_kernel<64, 32, 2, 2, 6, dense, three slabs per step> (dense fp8, 64 x 32 tiles, split-K 7)",
                 "kernel_avg_us": round(avg_us, 3),
                 "kernel_timing": "back-to-back launches in one graph, events around it / launches",
                 "launches": args.kernel_launches,

@@ -123,6 +123,9 @@ const Config* configs(int* count) {
       // skinny M: split-K over workgroups
       make_config<64, 64, 1, 4, 8, dg::kDense>("dense_64x64_w4_s8"),
       make_config<64, 32, 2, 2, 4, dg::kDense>("dense_64x32_w4_s4"),
+      // the same tile consuming two or three slabs per barrier step
+      make_config<64, 32, 2, 2, 4, dg::kDense, dg::kPair>("dense_64x32_w4_s4_pair"),
+      make_config<64, 32, 2, 2, 6, dg::kDense, dg::kTriple>("dense_64x32_w4_s6_triple"),
       // contiguous (block rows <= the 128-row alignment)
       make_config<128, 256, 2, 4, 3, dg::kContiguous>("contig_128x256_w8_s3"),
       make_config<128, 128, 2, 2, 3, dg::kContiguous>("contig_128x128_w4_s3"),
@@ -583,9 +586,15 @@ const Config* dense_default_config(int dtype, int m, int n, int kb, const Device
       // m <= 64: 64 x 32 tiles up to N 4096, and up to N 8192 while K is
       // short (at most 16 slabs): 64 x 7168 x 2048 in 10.0 against 11.3 us
       // for 64 x 64, which leads at long K (64 x 7168 x 16384: 34.0 against
-      // 41.0 us) and at N 24576 (13.0 against 13.5 us).
+      // 41.0 us) and at N 24576 (13.0 against 13.5 us).  The 64 x 32 tile
+      // consumes three slabs per barrier step (six stages): its steps are
+      // latency chains, not bandwidth (back to back, us, one slab per step
+      // against three: 64 x 2112 x 7168 10.50 / 10.07, 32 x 2112 x 7168
+      // 10.33 / 9.56, 64 x 4096 x 7168 14.18 / 12.88, 64 x 576 x 7168
+      // 8.45 / 7.92, 64 x 7168 x 2048 9.33 / 8.88, 64 x 512 x 1024 5.06 /
+      // 4.94).
       if (m <= 64)
-        return find_config(n <= 4096 || (kb <= 16 && n <= 8192) ? "dense_64x32_w4_s4" : "dense_64x64_w4_s3",
+        return find_config(n <= 4096 || (kb <= 16 && n <= 8192) ? "dense_64x32_w4_s6_triple" : "dense_64x64_w4_s3",
                            dg::kDense);
       // large: the 128 x 256 one-B-buffer tile, two workgroups per CU.  Medians
       // of five alternating runs against 256 x 256: 4096 x 7168 x 16384 467
@@ -602,7 +611,8 @@ const Config* dense_default_config(int dtype, int m, int n, int kb, const Device
       // 2112 x 7168: 13.8 against 15.5 us).
       if (few || (m <= 128 && t128 <= 128 && kb <= 12)) {
         const bool narrow = n <= 1024 || (m <= 128 && t128 <= 64 && kb <= 16);
-        return find_config(narrow ? "dense_64x32_w4_s4" : "dense_64x64_w4_s3", dg::kDense);
+        // three slabs per step here too: 128 x 2112 x 1024 in 5.96 against 6.20 us
+        return find_config(narrow ? "dense_64x32_w4_s6_triple" : "dense_64x64_w4_s3", dg::kDense);
       }
       if (t128 <= 72 && n >= 1024) return find_config("dense_128x128_w4_s3", dg::kDense);
       // short K (at most 12 slabs) where the two-per-CU tile would be split

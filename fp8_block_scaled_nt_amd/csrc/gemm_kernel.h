@@ -337,6 +337,17 @@ __device__ __forceinline__ int loads_ahead(int kb, int KB) {
   return n < NST - 2 ? n : NST - 2;
 }
 
+// The same for steps of STEP slabs (kPair, kTriple): at the top of the step
+// that consumes slabs kb .. kb+STEP-1, the batches issued after the last of
+// them (the prologue issues slabs 0..NST-1-STEP, step kb issues
+// kb+NST-STEP .. kb+NST-1).
+template <int NST, int STEP>
+__device__ __forceinline__ int loads_ahead_step(int kb, int KB) {
+  const int hi = KB < kb + NST - STEP ? KB : kb + NST - STEP;
+  const int lo = KB < kb + STEP ? KB : kb + STEP;
+  return hi > lo ? hi - lo : 0;
+}
+
 // LDS slot swizzle of tile row r (see the layout note at the top)
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
@@ -347,7 +358,7 @@ __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 // slab into registers first, and the next slab's B is loaded over them after
 // a second barrier; the smaller LDS footprint fits two workgroups per CU,
 // whose phases then overlap).
-enum Schedule { kInterleaved = 0, kPingPong = 1, kSingleB = 2 };
+enum Schedule { kInterleaved = 0, kPingPong = 1, kSingleB = 2, kPair = 3, kTriple = 4 };
 
 template <int BM, int BN, int WM, int WN, int NST, int VAR, int SCHED = kInterleaved, int DT = kFp8,
           int EPI = kEpiBf16>
@@ -360,6 +371,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   constexpr int kJb = BN / 8;
   constexpr int kSps = DT == kFp4 ? 2 : 1;  // scale slabs per 128-byte slab
   constexpr bool kSB = SCHED == kSingleB;
+  // slabs consumed per barrier step of the interleaved loop: kPair takes two,
+  // halving the dependent wait / barrier / fragment-read / MFMA steps of a
+  // workgroup that has few slabs and tiny tiles (decode shapes)
+  constexpr int kStep = SCHED == kPair ? 2 : SCHED == kTriple ? 3 : 1;
+  static_assert(kStep == 1 || (NST % kStep == 0 && NST >= 2 * kStep && DT == kFp8 && EPI == kEpiBf16 && VAR == kDense),
+                "multi-slab steps: dense fp8, stages a multiple of (and at least twice) the step");
   using S = Smem<BM, BN, NST, kSps, kSB>;
   static_assert(!kSB || NST == 2, "one B buffer: the next slab's B lands while this one is computed");
   static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be whole fragments");
@@ -805,24 +822,32 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
       end_step();
     }
   } else {
-    // ---- prologue: DMA of slabs 0..NST-2
+    // ---- prologue: DMA of slabs 0..NST-1-kStep
     #pragma unroll
-    for (int s0 = 0; s0 <= NST - 2; ++s0)
+    for (int s0 = 0; s0 <= NST - 1 - kStep; ++s0)
       if (s0 < KB) issue_slab(s0, s0);
 
     // the main loop, compiled once per B scale split (kSplit: fragments of
     // this wave in the first block; FN when all are in one)
     auto main_loop = [&](auto split_c) {
     constexpr int kSplit = decltype(split_c)::value;
-    for (int kb = 0; kb < KB; ++kb) {
-      // slab kb's DMA must have landed (in every wave: then the barrier); the
-      // loads issued after it may stay in flight.
-      wait_vmem_dyn(kVmPerDma * c_loads * loads_ahead<NST>(kb, KB));
-      block_barrier();  // also: every wave is done with the stage about to be refilled
+    for (int kb2 = 0; kb2 < KB; kb2 += kStep) {
+      // the step's slabs (kb2, and kb2+1 for kPair) must have landed (in
+      // every wave: then the barrier); the loads issued after them may stay
+      // in flight.
+      wait_vmem_dyn(kVmPerDma * c_loads *
+                    (kStep == 1 ? loads_ahead<NST>(kb2, KB) : loads_ahead_step<NST, kStep>(kb2, KB)));
+      block_barrier();  // also: every wave is done with the stages about to be refilled
       __builtin_amdgcn_sched_barrier(0);
-      if (!kSB && kb + NST - 1 < KB) issue_slab(kb + NST - 1, (kb + NST - 1) % NST);
+      #pragma unroll
+      for (int q = 0; q < kStep; ++q)
+        if (!kSB && kb2 + NST - kStep + q < KB) issue_slab(kb2 + NST - kStep + q, (kb2 + NST - kStep + q) % NST);
       __builtin_amdgcn_sched_barrier(0);
 
+    #pragma unroll
+    for (int sub = 0; sub < kStep; ++sub) {
+      const int kb = kb2 + sub;
+      if (kStep > 1 && kb >= KB) break;
       const uint8_t* st = smem + (kb % NST) * S::kStage;
       const uint8_t* sA = st;
       const uint8_t* sB = kSB ? smem + S::kBShared : st + S::kA;
@@ -960,6 +985,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+    }
     }
     };
     if constexpr (kSbUniform || DT != kFp8) {

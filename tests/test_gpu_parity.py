@@ -24,7 +24,8 @@ pytestmark = pytest.mark.gpu
 DENSE_CONFIGS = ["dense_256x256_w8_s2", "dense_256x128_w8_s3", "dense_128x256_w8_s3", "dense_128x128_w4_s3",
                  "dense_128x128_w4_s2", "dense_64x64_w4_s3", "dense_64x64_w4_s8", "dense_64x32_w4_s4", "dense_256x224_w8_s2",
                  "dense_128x256_w4_s3_wide", "dense_256x256_w8_s2_pp", "dense_256x128_w4_s2",
-                 "dense_256x128_w4_s3", "dense_128x256_w4_s3", "dense_128x256_w4_s2_sb"]
+                 "dense_256x128_w4_s3", "dense_128x256_w4_s3", "dense_128x256_w4_s2_sb",
+                 "dense_64x32_w4_s4_pair", "dense_64x32_w4_s6_triple"]
 
 
 def dense_case(m, n, k, seed, b_std=1.0):
@@ -308,7 +309,7 @@ def test_dense_long_k_pipeline(gpu):
     (64, 130, 1408, "11"),    # more splits than one batch of the reducer's partial loads
 ])
 @pytest.mark.parametrize("cfg", ["dense_64x64_w4_s8", "dense_64x32_w4_s4", "dense_128x128_w4_s2",
-                                 "dense_128x256_w4_s2_sb"])
+                                 "dense_128x256_w4_s2_sb", "dense_64x32_w4_s6_triple", "dense_64x32_w4_s4_pair"])
 def test_dense_split_k(gpu, m, n, k, splits, cfg, monkeypatch):
     if splits:
         monkeypatch.setenv("DG_SPLIT_K", splits)
@@ -340,7 +341,8 @@ def test_dense_default_mid_shapes(gpu, m, n, k):
     assert np.array_equal(H.d_bits(d), H.d_bits(d2))
 
 
-@pytest.mark.parametrize("cfg", ["dense_64x64_w4_s8", "dense_64x32_w4_s4", "dense_128x128_w4_s2"])
+@pytest.mark.parametrize("cfg", ["dense_64x64_w4_s8", "dense_64x32_w4_s4", "dense_128x128_w4_s2",
+                                 "dense_64x32_w4_s6_triple"])
 def test_split_k_back_to_back_shapes(gpu, cfg, monkeypatch):
     # calls with different split counts and tile counts in a row share the workspace
     monkeypatch.setenv("DG_FORCE_CONFIG", cfg)

@@ -61,7 +61,7 @@ def small_m_shapes(count):
 
 
 @pytest.mark.parametrize("m,n,kslabs", small_m_shapes(6))
-@pytest.mark.parametrize("cfg", [None, "skinny_64x32_w16_stagea", "dense_64x32_w4_s4"])
+@pytest.mark.parametrize("cfg", [None, "skinny_64x32_w16_stagea", "dense_64x32_w4_s4", "dense_64x32_w4_s6_triple"])
 def test_random_small_m(gpu, m, n, kslabs, cfg, monkeypatch):
     if cfg:
         monkeypatch.setenv("DG_FORCE_CONFIG", cfg)

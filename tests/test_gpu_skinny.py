@@ -86,7 +86,7 @@ def _device_operands(case, gpu):
             H.codes_to_device(qb, gpu), H.f32_to_device(sb, gpu))
 
 
-@pytest.mark.parametrize("cfg", ["skinny_64x32_w16_stagea", "dense_64x32_w4_s4"])
+@pytest.mark.parametrize("cfg", ["skinny_64x32_w16_stagea", "dense_64x32_w4_s4", "dense_64x32_w4_s6_triple"])
 def test_two_streams_overlap(gpu, cfg, monkeypatch):
     """Two split-K calls of the decode shape enqueued on two streams with no
     synchronisation between them (each stream has its own workspace): both
