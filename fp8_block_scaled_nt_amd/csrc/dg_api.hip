@@ -126,6 +126,7 @@ const Config* configs(int* count) {
       // the same tile consuming two or three slabs per barrier step
       make_config<64, 32, 2, 2, 4, dg::kDense, dg::kPair>("dense_64x32_w4_s4_pair"),
       make_config<64, 32, 2, 2, 6, dg::kDense, dg::kTriple>("dense_64x32_w4_s6_triple"),
+      make_config<64, 64, 1, 4, 4, dg::kDense, dg::kPair>("dense_64x64_w4_s4_pair"),
       // contiguous (block rows <= the 128-row alignment)
       make_config<128, 256, 2, 4, 3, dg::kContiguous>("contig_128x256_w8_s3"),
       make_config<128, 128, 2, 2, 3, dg::kContiguous>("contig_128x128_w4_s3"),
@@ -594,7 +595,7 @@ const Config* dense_default_config(int dtype, int m, int n, int kb, const Device
       // 8.45 / 7.92, 64 x 7168 x 2048 9.33 / 8.88, 64 x 512 x 1024 5.06 /
       // 4.94).
       if (m <= 64)
-        return find_config(n <= 4096 || (kb <= 16 && n <= 8192) ? "dense_64x32_w4_s6_triple" : "dense_64x64_w4_s3",
+        return find_config(n <= 4096 || (kb <= 16 && n <= 8192) ? "dense_64x32_w4_s6_triple" : "dense_64x64_w4_s4_pair",
                            dg::kDense);
       // large: the 128 x 256 one-B-buffer tile, two workgroups per CU.  Medians
       // of five alternating runs against 256 x 256: 4096 x 7168 x 16384 467
@@ -611,8 +612,13 @@ const Config* dense_default_config(int dtype, int m, int n, int kb, const Device
       // 2112 x 7168: 13.8 against 15.5 us).
       if (few || (m <= 128 && t128 <= 128 && kb <= 12)) {
         const bool narrow = n <= 1024 || (m <= 128 && t128 <= 64 && kb <= 16);
-        // three slabs per step here too: 128 x 2112 x 1024 in 5.96 against 6.20 us
-        return find_config(narrow ? "dense_64x32_w4_s6_triple" : "dense_64x64_w4_s3", dg::kDense);
+        // multi-slab steps here too: 128 x 2112 x 1024 in 5.96 against 6.20 us
+        // (64 x 32, three per step); 64 x 64 with two per step and four
+        // stages against three stages one per step: 128 x 16384 x 1024 9.00
+        // against 9.99, 128 x 12288 x 1536 11.69 against 12.37, 64 x 24576 x
+        // 1536 12.53 against 12.89, 64 x 7168 x 16384 32.6 against 33.0,
+        // 64 x 8192 x 7168 18.5 against 18.9 us
+        return find_config(narrow ? "dense_64x32_w4_s6_triple" : "dense_64x64_w4_s4_pair", dg::kDense);
       }
       if (t128 <= 72 && n >= 1024) return find_config("dense_128x128_w4_s3", dg::kDense);
       // short K (at most 12 slabs) where the two-per-CU tile would be split

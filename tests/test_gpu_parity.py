@@ -25,7 +25,7 @@ DENSE_CONFIGS = ["dense_256x256_w8_s2", "dense_256x128_w8_s3", "dense_128x256_w8
                  "dense_128x128_w4_s2", "dense_64x64_w4_s3", "dense_64x64_w4_s8", "dense_64x32_w4_s4", "dense_256x224_w8_s2",
                  "dense_128x256_w4_s3_wide", "dense_256x256_w8_s2_pp", "dense_256x128_w4_s2",
                  "dense_256x128_w4_s3", "dense_128x256_w4_s3", "dense_128x256_w4_s2_sb",
-                 "dense_64x32_w4_s4_pair", "dense_64x32_w4_s6_triple"]
+                 "dense_64x32_w4_s4_pair", "dense_64x32_w4_s6_triple", "dense_64x64_w4_s4_pair"]
 
 
 def dense_case(m, n, k, seed, b_std=1.0):
