@@ -142,16 +142,21 @@ class ClockSampler:
         if self.handle is None:
             return self
         self._stop = threading.Event()
+        first = threading.Event()
 
         def run():
             while not self._stop.is_set():
                 v = self.read_mhz()
                 if v is not None:
                     self.samples.append(v)
+                first.set()
                 time.sleep(0.0005)
 
         self._thread = threading.Thread(target=run, daemon=True)
         self._thread.start()
+        # the thread's start-up and first (slowest) query stay out of the
+        # timed region that follows
+        first.wait(1.0)
         return self
 
     def __exit__(self, *exc):
@@ -645,6 +650,7 @@ def main():
     g_warm.replay()
     torch.cuda.synchronize()
     with CLOCK:
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
         g_main.replay()
         torch.cuda.synchronize()
