@@ -708,17 +708,14 @@ bool skinny_plan(const SkinnyConfig* c, int m, int n, int kb, const DeviceInfo* 
 }
 
 // The skinny configuration a dense fp8 call uses (nullptr: the tiled kernels):
-// DG_FORCE_CONFIG when it names a skinny configuration (then m must be at
-// most 64), else skinny_64x32_w16_stagea for m <= 16 while one run of units
-// per CU covers the shape and each run keeps at least 12 of its 16 waves
-// busy.  Measured (kernel time with events, median, m 1-16): N 2112 K 7168
-// 9.4-9.6 against 10.9-11.2 us for the tiled split-K kernel, N 7168 K 2048
-// 8.7-8.9 against 9.8-9.9 us (14 units per run); with fewer units per run
-// the partial-tile hand-off dominates: N 576 K 7168 (4 per run) 11.0
-// against 8.7 us, N 512 K 1024 (1 per run) 8.4 against 5.3 us.  At m 32
-// it is level, at m 48 and 64 behind (11.6 and 12.1 against 11.0 and
-// 10.8 us on N 2112), where reloading A in every run costs more than the
-// tiled kernel's pipelined LDS staging.
+// only DG_FORCE_CONFIG naming a skinny configuration (then m must be at most
+// 64).  The skinny kernel used to be the default for m <= 16 (N 2112 K 7168
+// in 9.4-9.6 against 10.9-11.2 us for the tiled split-K kernel of the time);
+// since the tiled 64 x 32 kernel takes three slabs per step it is ahead at
+// every m <= 16 shape measured (back to back, us, skinny / tiled): 8 x 2112
+// x 7168 9.87 / 9.52, 1 x 2112 x 7168 9.82 / 9.38, 16 x 2112 x 7168 10.04 /
+// 9.52, 8 x 7168 x 2048 9.09 / 8.28, 16 x 7168 x 2048 9.28 / 8.31, 4 x 576
+// x 7168 11.23 / 7.75, 16 x 4096 x 7168 17.16 / 11.47.
 int skinny_config(int m, int n, int kb, const DeviceInfo* info, SkinnyPlan* plan) {
   plan->c = nullptr;
   const char* e = getenv("DG_FORCE_CONFIG");
@@ -729,10 +726,7 @@ int skinny_config(int m, int n, int kb, const DeviceInfo* info, SkinnyPlan* plan
       return fail(DG_ERR_INVALID_ARGUMENT, "configuration %s does not take m=%d n=%d k=%d", e, m, n, kb * 128);
     return DG_OK;
   }
-  SkinnyPlan pl;
-  if (m <= 16 && skinny_plan(find_skinny("skinny_64x32_w16_stagea"), m, n, kb, info, &pl) && pl.grid <= info->cus &&
-      pl.per >= 12)
-    *plan = pl;
+  (void)m; (void)n; (void)kb; (void)info;
   return DG_OK;
 }
 

@@ -122,8 +122,8 @@ def test_workspace_size_then_graph_of_mid_shape(gpu):
     assert dg.dense_workspace_size(4096, 7168, 16384) == 0                       # 448 big tiles, no split
     assert dg.dense_workspace_size(4096, 896, 16384) == 224 * 2 * 128 * 128 * 4  # 128 x 128 tiles, 2 splits
     assert dg.dense_workspace_size(0, 896, 16384) == 0
-    # m <= 16: the skinny kernel, 64 x 32 tiles with at most 5 contributors each
-    assert dg.dense_workspace_size(16, 2112, 7168) == 66 * 5 * tile
+    # m <= 16: the same tiled kernel, 64 x 32 tiles, 7 splits
+    assert dg.dense_workspace_size(16, 2112, 7168) == 66 * 7 * tile
     m, n, k = 1024, 896, 2048  # 56 tiles of 128 x 128, 8 splits
     need = dg.dense_workspace_size(m, n, k)
     assert need == 56 * 8 * 128 * 128 * 4

@@ -48,7 +48,7 @@ def test_random_dense(gpu, m, n, kslabs):
 
 def small_m_shapes(count):
     """Decode-like shapes: m 1..16 and N x K with 3100-4000 units of a 64x32
-    tile and a 128-wide slab, the range where the skinny kernel is the default."""
+    tile and a 128-wide slab, the range the skinny kernel was written for."""
     rng = np.random.default_rng(RNG_SEED + 16)
     out = []
     for _ in range(count):

@@ -118,8 +118,8 @@ def test_dense_decode_full(gpu):
 
 
 def test_dense_decode_small_batch_full(gpu):
-    # m = 8: the skinny split-K kernel's default shape
-    assert dg.dense_workspace_size(8, 2112, 7168) == 66 * 5 * 64 * 32 * 4
+    # m = 8: 64 x 32 tiles with 8 valid rows, split 7 ways
+    assert dg.dense_workspace_size(8, 2112, 7168) == 66 * 7 * 64 * 32 * 4
     dense_case(gpu, "dense_decode_8x2112x7168", whole=True)
 
 

@@ -54,9 +54,11 @@ SKINNY_TILE_BYTES = 64 * 32 * 4  # one fp32 partial tile of the skinny kernel
     # tiled split-K with 64 x 32 tiles on a small dense shape, then smaller
     [(128, 512, 1024, 1.0), (96, 200, 512, 1.0)],
 ], ids=["skinny", "tiled-decode", "tiled-small"])
-def test_noalloc_matches_default_entry_point(gpu, shapes):
+def test_noalloc_matches_default_entry_point(gpu, shapes, monkeypatch):
     if shapes[0][0] <= 16:
-        # the skinny plans: 66 and 57 tiles of 64 x 32, 5 and 6 partial slots each
+        # the skinny split-K kernel, by name (the tiled kernel is the default
+        # at these sizes): 66 and 57 tiles of 64 x 32, 5 and 6 partial slots each
+        monkeypatch.setenv("DG_FORCE_CONFIG", "skinny_64x32_w16_stagea")
         assert dg.dense_workspace_size(8, 2112, 7168) == 66 * 5 * SKINNY_TILE_BYTES
         assert dg.dense_workspace_size(5, 1800, 7168) == 57 * 6 * SKINNY_TILE_BYTES
     for i, (m, n, k, b_std) in enumerate(shapes):

@@ -38,9 +38,8 @@ WORKLOADS = {
     "dense_decode_64x2112x7168": Workload(
         "dense_decode_64x2112x7168", "dense", "dense decode-shaped GEMM (M=64 N=2112 K=7168)",
         m=64, n=2112, k=7168, b_std=0.02),
-    # The decode shape at a small batch (8 rows), where the skinny split-K
-    # kernel is the default; an extra line beside the pages' shapes, not one
-    # of them
+    # The decode shape at a small batch (8 rows); an extra line beside the
+    # pages' shapes, not one of them
     "dense_decode_8x2112x7168": Workload(
         "dense_decode_8x2112x7168", "dense", "dense decode-shaped GEMM, 8 rows (M=8 N=2112 K=7168)",
         m=8, n=2112, k=7168, b_std=0.02),
