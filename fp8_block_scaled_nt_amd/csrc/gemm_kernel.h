@@ -375,8 +375,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_nt_kernel(GemmParams p)
   // halving the dependent wait / barrier / fragment-read / MFMA steps of a
   // workgroup that has few slabs and tiny tiles (decode shapes)
   constexpr int kStep = SCHED == kPair ? 2 : SCHED == kTriple ? 3 : 1;
-  static_assert(kStep == 1 || (NST % kStep == 0 && NST >= 2 * kStep && DT == kFp8 && EPI == kEpiBf16 && VAR == kDense),
-                "multi-slab steps: dense fp8, stages a multiple of (and at least twice) the step");
+  static_assert(kStep == 1 || (NST % kStep == 0 && NST >= 2 * kStep && EPI == kEpiBf16 && VAR == kDense),
+                "multi-slab steps: dense, stages a multiple of (and at least twice) the step");
   using S = Smem<BM, BN, NST, kSps, kSB>;
   static_assert(!kSB || NST == 2, "one B buffer: the next slab's B lands while this one is computed");
   static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be whole fragments");

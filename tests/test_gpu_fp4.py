@@ -25,7 +25,7 @@ from tests import gpu_harness as H
 
 pytestmark = pytest.mark.gpu
 
-FP4_CONFIGS = ["fp4_256x256_w8_s2", "fp4_128x128_w4_s2", "fp4_64x32_w4_s4", "fp4_64x64_w4_s3"]
+FP4_CONFIGS = ["fp4_256x256_w8_s2", "fp4_128x128_w4_s2", "fp4_64x32_w4_s4", "fp4_64x64_w4_s3", "fp4_64x32_w4_s6_triple"]
 
 
 def with_ties(x):
@@ -100,9 +100,10 @@ def test_fp4_every_config(gpu, cfg, m, n, k, monkeypatch):
     check_fp4(gpu, *fp4_case(m, n, k, seed=3), label=f"{cfg} {m}x{n}x{k}")
 
 
+@pytest.mark.parametrize("cfg", ["fp4_64x32_w4_s4", "fp4_64x32_w4_s6_triple"])
 @pytest.mark.parametrize("splits", [2, 3, 5])
-def test_fp4_forced_split_k(gpu, splits, monkeypatch):
-    monkeypatch.setenv("DG_FORCE_CONFIG", "fp4_64x32_w4_s4")
+def test_fp4_forced_split_k(gpu, splits, cfg, monkeypatch):
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
     monkeypatch.setenv("DG_SPLIT_K", str(splits))
     d, _ = check_fp4(gpu, *fp4_case(64, 200, 2560, seed=splits), label=f"fp4 split-K {splits}")
     d2, _ = H.run_fp4(*fp4_case(64, 200, 2560, seed=splits), gpu)
