@@ -357,7 +357,10 @@ __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 // interleaved loop with one B buffer: every wave reads its B fragments of a
 // slab into registers first, and the next slab's B is loaded over them after
 // a second barrier; the smaller LDS footprint fits two workgroups per CU,
-// whose phases then overlap).
+// whose phases then overlap), or kPair / kTriple (the interleaved loop
+// consuming two or three slabs per barrier step, for small tiles whose slab
+// steps are latency chains rather than bandwidth: one wait, one barrier and
+// one refill per step).
 enum Schedule { kInterleaved = 0, kPingPong = 1, kSingleB = 2, kPair = 3, kTriple = 4 };
 
 template <int BM, int BN, int WM, int WN, int NST, int VAR, int SCHED = kInterleaved, int DT = kFp8,
