@@ -153,6 +153,7 @@ const Config* configs(int* count) {
       make_config<256, 256, 2, 4, 2, dg::kDense, dg::kInterleaved, dg::kBf16>("bf16_256x256_w8_s2"),
       make_config<128, 128, 2, 2, 2, dg::kDense, dg::kInterleaved, dg::kBf16>("bf16_128x128_w4_s2"),
       make_config<64, 32, 2, 2, 4, dg::kDense, dg::kInterleaved, dg::kBf16>("bf16_64x32_w4_s4"),
+      make_config<64, 32, 2, 2, 4, dg::kDense, dg::kPair, dg::kBf16>("bf16_64x32_w4_s4_pair"),
       make_config<64, 64, 1, 4, 3, dg::kDense, dg::kInterleaved, dg::kBf16>("bf16_64x64_w4_s3"),
       // FP4 (e2m1) dense (selected the same way by dtype)
       make_config<256, 256, 2, 4, 2, dg::kDense, dg::kInterleaved, dg::kFp4>("fp4_256x256_w8_s2"),
@@ -560,9 +561,13 @@ const Config* dense_default_config(int dtype, int m, int n, int kb, const Device
       // 16.7 against 24.4).
       if (m <= 64) {
         const bool narrow = n <= 4096 || (n <= 8192 && kb <= 32);
-        return find_config(narrow ? "bf16_64x32_w4_s4" : "bf16_64x64_w4_s3", dg::kDense, dg::kBf16);
+        // two slabs per step (four stages): 16 x 2112 x 7168 in 12.9 against
+        // 14.7 us, 64 x 4096 x 7168 18.7 against 21.7, 64 x 7168 x 2048 12.5
+        // against 13.9, 64 x 2112 x 7168 level (13.5); three slabs per step
+        // lost at 64 x 2112 x 7168 (14.0)
+        return find_config(narrow ? "bf16_64x32_w4_s4_pair" : "bf16_64x64_w4_s3", dg::kDense, dg::kBf16);
       }
-      if (few && n <= 1024) return find_config("bf16_64x32_w4_s4", dg::kDense, dg::kBf16);
+      if (few && n <= 1024) return find_config("bf16_64x32_w4_s4_pair", dg::kDense, dg::kBf16);
       if ((few && n <= 4096) || (m <= 128 && kb <= 32)) return find_config("bf16_64x64_w4_s3", dg::kDense, dg::kBf16);
       return find_config(mid ? "bf16_128x128_w4_s2" : "bf16_256x256_w8_s2", dg::kDense, dg::kBf16);
     case dg::kFp4:

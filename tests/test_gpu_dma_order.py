@@ -62,8 +62,11 @@ def _fp4(dev):
     (_fp8, "dense_64x64_w4_s3"),
     (_fp8, "dense_64x64_w4_s4_pair"),
     (_bf16, "bf16_64x32_w4_s4"),
+    (_bf16, "bf16_64x32_w4_s4_pair"),
     (_fp4, "fp4_64x32_w4_s4"),
-], ids=["fp8-64x32", "fp8-64x32-triple", "fp8-64x64", "fp8-64x64-pair", "bf16-64x32", "fp4-64x32"])
+    (_fp4, "fp4_64x32_w4_s6_triple"),
+], ids=["fp8-64x32", "fp8-64x32-triple", "fp8-64x64", "fp8-64x64-pair", "bf16-64x32", "bf16-64x32-pair",
+        "fp4-64x32", "fp4-64x32-triple"])
 def test_repeated_calls_same_bits(gpu, make, cfg, monkeypatch):
     monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
     monkeypatch.setenv("DG_SPLIT_K", "1")

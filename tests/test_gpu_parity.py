@@ -402,7 +402,7 @@ def bf16_bits(x):
 
 
 @pytest.mark.parametrize("cfg", [None, "bf16_256x256_w8_s2", "bf16_128x128_w4_s2", "bf16_64x32_w4_s4",
-                                 "bf16_64x64_w4_s3"])
+                                 "bf16_64x64_w4_s3", "bf16_64x32_w4_s4_pair"])
 @pytest.mark.parametrize("m,n,k", [(300, 520, 640), (64, 2112, 1024), (1, 16, 64), (520, 300, 128),
                                    (200, 2112, 512)])
 def test_bf16_gemm(gpu, cfg, m, n, k, monkeypatch):
@@ -433,8 +433,9 @@ def test_bf16_default_tile_regions(gpu, m, n, k):
     assert H.guard_untouched(flat, d.numel())
 
 
-def test_bf16_gemm_forced_split_k(gpu, monkeypatch):
-    monkeypatch.setenv("DG_FORCE_CONFIG", "bf16_64x32_w4_s4")
+@pytest.mark.parametrize("cfg", ["bf16_64x32_w4_s4", "bf16_64x32_w4_s4_pair"])
+def test_bf16_gemm_forced_split_k(gpu, cfg, monkeypatch):
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
     monkeypatch.setenv("DG_SPLIT_K", "5")
     m, n, k = 48, 200, 1280
     x = W.draw_dense(m, n, k, seed=3)
