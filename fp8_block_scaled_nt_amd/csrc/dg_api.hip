@@ -161,6 +161,7 @@ const Config* configs(int* count) {
       make_config<64, 32, 2, 2, 4, dg::kDense, dg::kInterleaved, dg::kFp4>("fp4_64x32_w4_s4"),
       make_config<64, 32, 2, 2, 6, dg::kDense, dg::kTriple, dg::kFp4>("fp4_64x32_w4_s6_triple"),
       make_config<64, 64, 1, 4, 3, dg::kDense, dg::kInterleaved, dg::kFp4>("fp4_64x64_w4_s3"),
+      make_config<64, 64, 1, 4, 4, dg::kDense, dg::kPair, dg::kFp4>("fp4_64x64_w4_s4_pair"),
       // MoE FC1 + SwiGLU + FP8 requantisation, masked layout (a 256-column
       // tile = 128 gate + 128 up columns = one 128-wide block of h)
       make_config<256, 256, 2, 4, 2, dg::kMasked, dg::kPingPong, dg::kFp8, dg::kEpiSwigluFp8>("swiglu_256x256_w8_s2_pp"),
@@ -585,12 +586,15 @@ const Config* dense_default_config(int dtype, int m, int n, int kb, const Device
         // three slabs per step (six stages), as for fp8: 64 x 2112 x 7168 in
         // 8.62 against 8.85 us, 16 x 2112 x 7168 8.52 against 8.81, 64 x 7168
         // x 2048 7.07 against 7.44 (back to back)
-        return find_config(narrow ? "fp4_64x32_w4_s6_triple" : "fp4_64x64_w4_s3", dg::kDense, dg::kFp4);
+        // wider N or longer K: 64 x 64 with two slabs per step (four stages):
+        // 64 x 7168 x 16384 in 19.7 against 21.4 us, 64 x 24576 x 1536 9.05
+        // against 9.63, 128 x 7168 x 4096 11.8 against 13.5
+        return find_config(narrow ? "fp4_64x32_w4_s6_triple" : "fp4_64x64_w4_s4_pair", dg::kDense, dg::kFp4);
       }
       if ((few && n <= 1024) || (m <= 128 && t128 <= 64 && (n <= 4096 ? kb <= 28 : n <= 8192 && kb <= 8)))
         return find_config("fp4_64x32_w4_s6_triple", dg::kDense, dg::kFp4);
       if (few || (mid && t128 <= 72 && n >= 1024) || (m <= 128 && kb <= 8))
-        return find_config("fp4_64x64_w4_s3", dg::kDense, dg::kFp4);
+        return find_config("fp4_64x64_w4_s4_pair", dg::kDense, dg::kFp4);
       return find_config(mid ? "fp4_128x128_w4_s2" : "fp4_256x256_w8_s2", dg::kDense, dg::kFp4);
     default: {
       // m <= 64: 64 x 32 tiles up to N 4096, and up to N 8192 while K is

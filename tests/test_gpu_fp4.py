@@ -25,7 +25,8 @@ from tests import gpu_harness as H
 
 pytestmark = pytest.mark.gpu
 
-FP4_CONFIGS = ["fp4_256x256_w8_s2", "fp4_128x128_w4_s2", "fp4_64x32_w4_s4", "fp4_64x64_w4_s3", "fp4_64x32_w4_s6_triple"]
+FP4_CONFIGS = ["fp4_256x256_w8_s2", "fp4_128x128_w4_s2", "fp4_64x32_w4_s4", "fp4_64x64_w4_s3", "fp4_64x32_w4_s6_triple",
+               "fp4_64x64_w4_s4_pair"]
 
 
 def with_ties(x):
